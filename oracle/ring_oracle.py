@@ -1,0 +1,411 @@
+"""Plain, slow, obviously-correct CPU oracle for one device's share of Ring
+Attention, in float64 NumPy.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this module. It shares no
+code with the HIP library (no kernels, headers, helpers or tables); the only
+thing both sides use is the seeded input generator module, which holds no
+attention arithmetic.
+
+Pages cited (by title and section; the pages are web text on Ring Attention):
+
+  [UL] Ultralytics glossary, "Ring Attention" (Arabic edition), section
+       "How ring attention works": the N-step schedule, the four-device
+       single-process simulation, the remark that production kernels subtract
+       a running maximum, and the remark on striped token assignment.
+  [TS] troisinh.com, "Ring Attention -- K/V truyen vong giua GPU, context
+       trieu token": sections "Y tuong cot loi" (core idea: fixed Q, K/V
+       rotating, associative merge), "Tai sao no hoat dong" (why it works: the
+       online-softmax update of the running max and normaliser, output
+       rescaled the same way) and "Y nghia thuc te" (practical implications:
+       causal masking wastes about half of the FLOPs).
+  [JS] jisaku.com glossary, "Ring Attention (ring attention)": sections on the
+       processing flow (step t uses the block received at step t-1) and on
+       communication/compute overlap.
+  [AU] AI Understanding, "Sekvensparallellism och ringuppmarksamhet": sections
+       "Djupdykning" (each device owns a contiguous chunk of tokens) and
+       "Teknisk insikt" (online softmax makes blockwise equal to full
+       attention).
+
+Conventions
+  * Tensors are [batch, seq, heads, head_dim] (the shape convention of the
+    package call shown on the [JS] page).
+  * Query head h reads KV head floor(h * Hkv / Hq) (grouped-query attention;
+    the pages are silent, this is the plain reading).
+  * scale defaults to 1/sqrt(head_dim), applied to the scores before the
+    softmax ([UL] simulation divides the scores by the square root of dim).
+  * Causal: a key is visible to a query iff its global position is <= the
+    query's global position ([TS] "Y nghia thuc te": autoregressive masking).
+  * Layouts: "contiguous" -- block i holds tokens [i*B, (i+1)*B) ([AU]
+    "Djupdykning"); "striped" -- token t belongs to block t mod N at local
+    index floor(t / N) ([UL] closing remark: each device receives tokens
+    spread evenly over the sequence).
+  * A partial is (m, l, acc): m = max visible scaled score, l = sum of
+    exp(s - m), acc = sum of exp(s - m) * v. A row with no visible key has
+    the empty partial (-inf, 0, 0), which is the identity of the merge.
+
+Every function is pinned by tests under tests/ against values the pages fix,
+closed forms, invariants, brute force and library routines (see the
+docstrings). No function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Tile classes. The integer values are this module's own; tests compare the
+# HIP library's classes through an explicit mapping, not through shared code.
+SKIP = 0
+PARTIAL = 1
+FULL = 2
+
+_LAYOUTS = ("contiguous", "striped")
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(d): the [UL] simulation divides q.k by dim ** 0.5."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def kv_head_of(h: int, hq: int, hkv: int) -> int:
+    """KV head read by query head h: floor(h*Hkv/Hq) (groups of Hq/Hkv)."""
+    return (h * hkv) // hq
+
+
+def global_positions(layout: str, n_ring: int, block: int, block_len: int) -> np.ndarray:
+    """Global token positions of the block_len tokens of ring block `block`.
+
+    contiguous: [AU] "Djupdykning" -- each device owns one contiguous chunk,
+                so position = block*block_len + a.
+    striped:    [UL] "How ring attention works", closing remark on striping --
+                tokens are spread evenly: token t -> block t mod N, local index
+                t // N, so position = a*N + block.
+    Pinned by tests: positions of all blocks partition range(N*B) exactly.
+    """
+    if layout not in _LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
+    a = np.arange(block_len, dtype=np.int64)
+    if layout == "contiguous":
+        return block * block_len + a
+    return a * n_ring + block
+
+
+def ring_order(rank: int, n_ring: int) -> list[int]:
+    """Block visited at each step: j = (rank - step) mod N ([UL] simulation:
+    at each step the device uses the block that arrived from the previous
+    device; [JS] processing flow: step 0 is the device's own block)."""
+    return [(rank - s) % n_ring for s in range(n_ring)]
+
+
+def _visibility(q_pos: np.ndarray, k_pos: np.ndarray, causal: bool) -> np.ndarray:
+    """[Lq, Lk] boolean: key visible to query (causal: key pos <= query pos)."""
+    if not causal:
+        return np.ones((q_pos.size, k_pos.size), dtype=bool)
+    return k_pos[None, :] <= q_pos[:, None]
+
+
+# --------------------------------------------------------------------------
+# O1 -- the plain definition, global token order.
+# --------------------------------------------------------------------------
+
+def naive_attention(q, k, v, causal: bool, scale: float | None = None):
+    """O = softmax(scale * Q K^T [+ causal mask]) V over the whole sequence.
+
+    q: [B, S, Hq, d]; k, v: [B, S, Hkv, d], all in global token order.
+    Returns (out [B, S, Hq, d] float64, lse [B, S, Hq] float64).
+    This is exact attention, the result ring attention must reproduce
+    ([UL] opening paragraph: no approximation of attention; [TS] "Tai sao no
+    hoat dong": the softmax with the row max subtracted).
+    Pinned by: torch CPU scaled_dot_product_attention in float64 (tiny
+    shapes), closed forms (constant keys -> mean of V; causal row 0 -> V[0]),
+    the affine-V invariant.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    pos = np.arange(q.shape[1], dtype=np.int64)
+    return naive_attention_rows(q, pos, k, v, causal, scale)
+
+
+def naive_attention_rows(q_rows, q_pos, k, v, causal: bool, scale: float | None = None):
+    """O1 for a subset of query rows.
+
+    q_rows: [B, R, Hq, d] with global positions q_pos [R]; k, v: [B, S, Hkv, d]
+    in global order (key u has position u). Used for sampled-row parity at
+    sizes where the full product is too large for a CPU.
+    """
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    bsz, nrows, hq, d = q_rows.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    k_pos = np.arange(k.shape[1], dtype=np.int64)
+    out = np.zeros((bsz, nrows, hq, d))
+    lse = np.full((bsz, nrows, hq), -np.inf)
+    for b in range(bsz):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            kk, vv = k[b, :, g, :], v[b, :, g, :]
+            if causal:
+                # only keys up to the largest query position can be visible
+                kmax = int(q_pos.max()) + 1
+                kk, vv, kp = kk[:kmax], vv[:kmax], k_pos[:kmax]
+            else:
+                kp = k_pos
+            s = (q_rows[b, :, h, :] @ kk.T) * scale
+            vis = _visibility(q_pos, kp, causal)
+            s = np.where(vis, s, -np.inf)
+            mx = s.max(axis=1, keepdims=True)
+            has = np.isfinite(mx)
+            base = np.where(has, mx, 0.0)
+            e = np.where(vis, np.exp(s - base), 0.0)
+            den = e.sum(axis=1, keepdims=True)
+            safe = np.where(den > 0, den, 1.0)
+            out[b, :, h, :] = np.where(den > 0, (e / safe) @ vv, 0.0)
+            lse[b, :, h] = np.where(has[:, 0], base[:, 0] + np.log(safe[:, 0]), -np.inf)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# O2 -- blockwise ring with online-softmax merge (separate code from O1).
+# --------------------------------------------------------------------------
+
+def empty_partial(bsz: int, lq: int, hq: int, d: int):
+    """(-inf, 0, 0): the state before any block arrives. The [UL] simulation
+    starts numerator and denominator at zero; the running max starts at -inf
+    so that the first merge takes the block's own max."""
+    return (np.full((bsz, lq, hq), -np.inf), np.zeros((bsz, lq, hq)), np.zeros((bsz, lq, hq, d)))
+
+
+def block_partial(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = None):
+    """Partial (m, l, acc) of the local queries against one arriving K/V block.
+
+    [UL] "How ring attention works": each device keeps a running sum of the
+    exponentiated scores and a running sum of the weighted values; production
+    kernels subtract a running maximum before exponentiating. So for each query
+    row: m = max of visible scaled scores, l = sum exp(s - m),
+    acc = sum exp(s - m) v. A row with no visible key gets (-inf, 0, 0).
+
+    q: [B, Lq, Hq, d] with positions q_pos [Lq]; k, v: [B, Lk, Hkv, d] with
+    positions k_pos [Lk].
+    Pinned by: m equals the exact max of visible scores and 1 <= l <= #visible
+    (invariant); merged over all blocks equals O1 (brute force, SDPA).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    bsz, lq, hq, d = q.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    vis = _visibility(np.asarray(q_pos, np.int64), np.asarray(k_pos, np.int64), causal)
+    has = vis.any(axis=1)
+    m, l, acc = empty_partial(bsz, lq, hq, d)
+    for b in range(bsz):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            s = (q[b, :, h, :] @ k[b, :, g, :].T) * scale
+            s_vis = np.where(vis, s, -np.inf)
+            mrow = s_vis.max(axis=1)
+            base = np.where(has, mrow, 0.0)
+            p = np.where(vis, np.exp(s - base[:, None]), 0.0)
+            m[b, :, h] = np.where(has, mrow, -np.inf)
+            l[b, :, h] = p.sum(axis=1)
+            acc[b, :, h, :] = p @ v[b, :, g, :]
+    return m, l, acc
+
+
+def merge_partials(p1, p2):
+    """Online-softmax merge of two partials ([TS] "Tai sao no hoat dong"):
+        m = max(m1, m2)
+        l = exp(m1 - m) l1 + exp(m2 - m) l2
+        acc = exp(m1 - m) acc1 + exp(m2 - m) acc2   (output rescaled the same way)
+    A side whose m is -inf contributes a factor of exactly 0; if both are -inf
+    the result stays the empty partial (no NaN).
+    Pinned by: merge algebra (identity, merge(x, x), commutativity,
+    associativity) and ring == O1.
+    """
+    m1, l1, a1 = p1
+    m2, l2, a2 = p2
+    m = np.maximum(m1, m2)
+    fin = np.isfinite(m)
+    base = np.where(fin, m, 0.0)
+    f1 = np.where(np.isfinite(m1), np.exp(np.where(np.isfinite(m1), m1, 0.0) - base), 0.0)
+    f2 = np.where(np.isfinite(m2), np.exp(np.where(np.isfinite(m2), m2, 0.0) - base), 0.0)
+    l = f1 * l1 + f2 * l2
+    acc = f1[..., None] * a1 + f2[..., None] * a2
+    return np.where(fin, m, -np.inf), l, acc
+
+
+def finalize(state):
+    """Divide the accumulated numerator by the denominator at the end ([UL]
+    "How ring attention works"). Also returns lse = m + ln l (the statistic a
+    backward pass recomputes from, [TS] "Tai sao no hoat dong", blockwise
+    backward). Rows with l == 0 give out = 0 and lse = -inf."""
+    m, l, acc = state
+    pos = l > 0
+    safe = np.where(pos, l, 1.0)
+    out = np.where(pos[..., None], acc / safe[..., None], 0.0)
+    lse = np.where(pos, m + np.log(safe), -np.inf)
+    return out, lse
+
+
+def ring_state(q_share, k_blocks, v_blocks, rank: int, n_ring: int, layout: str,
+               causal: bool, scale: float | None = None, blocks=None, state=None):
+    """Running (m, l, acc) after visiting `blocks` (default: the ring order of
+    `rank`), starting from `state` (default: empty).
+
+    q_share: [B, Lq, Hq, d] -- the local query block, fixed for the whole ring
+    ([TS] "Y tuong cot loi"; [JS] ring structure). k_blocks, v_blocks:
+    [N, B, Lk, Hkv, d] -- block j holds the tokens the layout gives to block j.
+    Pinned by: the split-ring invariant (state after k steps merged with the
+    rest equals the whole ring).
+    """
+    q_share = _f64(q_share)
+    bsz, lq, hq, d = q_share.shape
+    q_pos = global_positions(layout, n_ring, rank, lq)
+    if blocks is None:
+        blocks = ring_order(rank, n_ring)
+    if state is None:
+        state = empty_partial(bsz, lq, hq, d)
+    lk = k_blocks.shape[2]
+    for j in blocks:
+        k_pos = global_positions(layout, n_ring, j, lk)
+        part = block_partial(q_share, q_pos, k_blocks[j], v_blocks[j], k_pos, causal, scale)
+        state = merge_partials(state, part)
+    return state
+
+
+def ring_share(q_share, k_blocks, v_blocks, rank: int, n_ring: int, layout: str,
+               causal: bool, scale: float | None = None, order=None):
+    """O2: one device's output after all N ring steps, (out, lse).
+
+    Steps follow ring_order(rank) unless `order` (any permutation of the N
+    blocks) is given; the result does not depend on it (merge is associative
+    and commutative, [TS] "Y tuong cot loi").
+    Pinned by: equality with O1 on the [UL] worked example and on brute-force
+    tiny cases, arrival-order invariance, torch SDPA.
+    """
+    return finalize(ring_state(q_share, k_blocks, v_blocks, rank, n_ring, layout,
+                               causal, scale, blocks=order))
+
+
+def ring_share_literal(q_share, k_blocks, v_blocks, rank: int, n_ring: int,
+                       scale: float | None = None):
+    """O2': the [UL] simulation's own formulation, non-causal, without max
+    subtraction: numerator += exp(s) v, denominator += sum exp(s), one divide at
+    the end. Exact in real arithmetic; used on small-score inputs only.
+    Pinned by: the [UL] printed result (matches full attention within 1e-5)."""
+    q_share = _f64(q_share)
+    bsz, lq, hq, d = q_share.shape
+    hkv = k_blocks.shape[3]
+    if scale is None:
+        scale = default_scale(d)
+    num = np.zeros((bsz, lq, hq, d))
+    den = np.zeros((bsz, lq, hq))
+    for j in ring_order(rank, n_ring):
+        kb, vb = _f64(k_blocks[j]), _f64(v_blocks[j])
+        for b in range(bsz):
+            for h in range(hq):
+                g = kv_head_of(h, hq, hkv)
+                e = np.exp((q_share[b, :, h, :] @ kb[b, :, g, :].T) * scale)
+                num[b, :, h, :] += e @ vb[b, :, g, :]
+                den[b, :, h] += e.sum(axis=1)
+    return num / den[..., None]
+
+
+# --------------------------------------------------------------------------
+# O3 -- integer references: tile classes and counted work.
+# --------------------------------------------------------------------------
+
+def tile_classes_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, j: int,
+                            q_len: int, kv_len: int, tq: int, tk: int) -> np.ndarray:
+    """[ceil(q_len/tq), ceil(kv_len/tk)] classes by counting visible elements.
+
+    A (q-tile, k-tile) pair is FULL when every in-bounds (query, key) pair of
+    it is visible, SKIP when none is, PARTIAL otherwise. Visibility uses global
+    positions of the local query share (block `rank`) and of block j.
+    Motivation: without skipping, causal ring attention spends about half its
+    FLOPs on masked pairs ([TS] "Y nghia thuc te"); devices holding early
+    queries skip most key blocks ([UL] closing remark).
+    """
+    q_pos = global_positions(layout, n_ring, rank, q_len)
+    k_pos = global_positions(layout, n_ring, j, kv_len)
+    vis = _visibility(q_pos, k_pos, causal)
+    nqt = -(-q_len // tq)
+    nkt = -(-kv_len // tk)
+    out = np.empty((nqt, nkt), dtype=np.int8)
+    for qt in range(nqt):
+        for kt in range(nkt):
+            t = vis[qt * tq:(qt + 1) * tq, kt * tk:(kt + 1) * tk]
+            cnt = int(t.sum())
+            out[qt, kt] = FULL if cnt == t.size else (SKIP if cnt == 0 else PARTIAL)
+    return out
+
+
+def tile_class_counts(layout: str, causal: bool, n_ring: int, rank: int, j: int,
+                      q_len: int, kv_len: int, tq: int, tk: int):
+    """(#FULL, #PARTIAL, #SKIP) without materialising elements, for real sizes.
+
+    For a fixed query, visible keys of a block form a prefix b <= lim(a)
+    (key positions increase with b), and lim is nondecreasing in a. A q-tile
+    [a0, a1] therefore sees k-tiles with b_hi <= lim(a0) fully, k-tiles with
+    b_lo > lim(a1) not at all, and the rest partially.
+    Pinned by: equality with tile_classes_bruteforce on small shapes.
+    """
+    q_pos = global_positions(layout, n_ring, rank, q_len)
+    k_pos = global_positions(layout, n_ring, j, kv_len)
+    nkt = -(-kv_len // tk)
+    full = part = skip = 0
+    for a0 in range(0, q_len, tq):
+        a1 = min(a0 + tq, q_len) - 1
+        if causal:
+            lim0 = int(np.searchsorted(k_pos, q_pos[a0], side="right")) - 1
+            lim1 = int(np.searchsorted(k_pos, q_pos[a1], side="right")) - 1
+        else:
+            lim0 = lim1 = kv_len - 1
+        # k-tiles fully visible: b_hi <= lim0 with b_hi = min((kt+1)tk, kv_len) - 1
+        n_full = 0 if lim0 < 0 else (lim0 + 1) // tk
+        if lim0 == kv_len - 1:
+            n_full = nkt
+        # k-tiles with any visible element: b_lo <= lim1
+        n_any = 0 if lim1 < 0 else lim1 // tk + 1
+        full += n_full
+        part += n_any - n_full
+        skip += nkt - n_any
+    return full, part, skip
+
+
+def visible_pairs_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, block_len: int) -> int:
+    """Number of visible (query, key) pairs of one device's share over all
+    blocks, counted element by element."""
+    q_pos = global_positions(layout, n_ring, rank, block_len)
+    total = 0
+    for j in range(n_ring):
+        total += int(_visibility(q_pos, global_positions(layout, n_ring, j, block_len), causal).sum())
+    return total
+
+
+def visible_pairs_closed_form(layout: str, causal: bool, n_ring: int, rank: int, block_len: int) -> int:
+    """Closed forms (per query head, per batch row):
+      non-causal: N B^2
+      contiguous causal: r B^2 + B(B+1)/2 (blocks j<r full, j=r triangle, j>r none)
+      striped causal: N B(B-1)/2 + (r+1) B (blocks j<=r keep the diagonal,
+                      blocks j>r lose it)
+    Pinned by: visible_pairs_bruteforce for many (N, B, r)."""
+    n, b, r = n_ring, block_len, rank
+    if not causal:
+        return n * b * b
+    if layout == "contiguous":
+        return r * b * b + b * (b + 1) // 2
+    return n * b * (b - 1) // 2 + (r + 1) * b
+
+
+def counted_flops(pairs: int, head_dim: int, hq: int, batch: int = 1) -> int:
+    """Algorithmic FLOPs: 2d for the score dot product plus 2d for the
+    weighted sum of V, per visible pair per query head. Exponentials, masked
+    elements and skipped tiles are not counted."""
+    return 4 * head_dim * hq * batch * pairs

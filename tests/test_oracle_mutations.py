@@ -1,0 +1,197 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant replaces one oracle function with a plausible wrong version (a
+dropped term, a wrong sign or index, a transposed operand). The pin battery
+below -- comparisons against torch's float64 SDPA, the Ultralytics worked
+example and closed forms, all computed without the oracle -- must fail for
+every mutant and pass for the unmutated oracle. Mistakes are planted only in
+the oracle, on the CPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ring_oracle as orc
+from tests.test_oracle_pins import _blocks_from_global, _rand, _sdpa64, _share_rows
+
+
+def _pins_hold() -> bool:
+    try:
+        # GQA, causal and non-causal, both layouts, vs float64 SDPA
+        for layout in ("contiguous", "striped"):
+            for causal in (False, True):
+                n, blen = 3, 4
+                q, k, v = _rand(7, 1, n * blen, 4, 2, 8)
+                q = 2.0 * q
+                ref = _sdpa64(q, k, v, causal)
+                out, lse = orc.naive_attention(q, k, v, causal)
+                if not np.allclose(out, ref, atol=1e-10, rtol=0):
+                    return False
+                kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+                for r in range(n):
+                    rows = _share_rows(layout, n, r, blen)
+                    o2, lse2 = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal)
+                    if not np.allclose(o2, ref[:, rows], atol=1e-10, rtol=0):
+                        return False
+                    if not np.allclose(lse2, lse[:, rows], atol=1e-10, rtol=0):
+                        return False
+                # counted work: closed form against an independent count
+                for r in range(n):
+                    rows = _share_rows(layout, n, r, blen)
+                    want = sum(1 for t in rows for u in range(n * blen) if (u <= t or not causal))
+                    if orc.visible_pairs_closed_form(layout, causal, n, r, blen) != want:
+                        return False
+                    for j in range(n):
+                        keys = _share_rows(layout, n, j, blen)
+                        c = orc.tile_classes_bruteforce(layout, causal, n, r, j, blen, blen, 2, 2)
+                        for qt in range(2):
+                            for kt in range(2):
+                                vis = [(u <= t or not causal) for t in rows[2 * qt:2 * qt + 2]
+                                       for u in keys[2 * kt:2 * kt + 2]]
+                                want_c = orc.FULL if all(vis) else (orc.SKIP if not any(vis) else orc.PARTIAL)
+                                if c[qt, kt] != want_c:
+                                    return False
+        # the page's literal (no max subtraction) form on its worked example size
+        q, k, v = _rand(0, 1, 32, 1, 1, 16)
+        kb, vb = _blocks_from_global(k, "contiguous", 4), _blocks_from_global(v, "contiguous", 4)
+        lit = np.concatenate([orc.ring_share_literal(q[:, 8 * i:8 * i + 8], kb, vb, i, 4)
+                              for i in range(4)], axis=1)
+        if not np.allclose(lit, _sdpa64(q, k, v, False), atol=1e-10, rtol=0):
+            return False
+        # merge: empty partial is the identity, and a scaled copy merges exactly
+        rng = np.random.default_rng(0)
+        m = rng.standard_normal((1, 3, 2))
+        l = rng.uniform(1, 2, (1, 3, 2))
+        acc = rng.standard_normal((1, 3, 2, 4))
+        x = (m, l, acc)
+        y = (m - 1.0, l, acc)
+        mm, ll, aa = orc.merge_partials(x, y)
+        if not (np.allclose(mm, m) and np.allclose(ll, l * (1 + math.exp(-1.0)))
+                and np.allclose(aa, acc * (1 + math.exp(-1.0)))):
+            return False
+        e = orc.empty_partial(1, 3, 2, 4)
+        mm, ll, aa = orc.merge_partials(e, x)
+        if not (np.array_equal(mm, m) and np.array_equal(ll, l) and np.array_equal(aa, acc)):
+            return False
+        return True
+    except (ValueError, IndexError, FloatingPointError):
+        return False
+
+
+def test_unmutated_oracle_passes_battery():
+    assert _pins_hold()
+
+
+def _mut_kv_head(h, hq, hkv):
+    return h % hkv
+
+
+def _mut_scale(d):
+    return 1.0 / d
+
+
+def _mut_positions_striped(layout, n_ring, block, block_len):
+    a = np.arange(block_len, dtype=np.int64)
+    if layout == "contiguous":
+        return block * block_len + a
+    return block * block_len + a  # striped treated as contiguous
+
+
+def _mut_positions_contiguous_off_by_one(layout, n_ring, block, block_len):
+    a = np.arange(block_len, dtype=np.int64)
+    if layout == "contiguous":
+        return block * (block_len - 1) + a  # blocks overlap by one position
+    return a * n_ring + block
+
+
+_orig_merge = orc.merge_partials
+_orig_block_partial = orc.block_partial
+_orig_visibility = orc._visibility
+_orig_finalize = orc.finalize
+_orig_literal = orc.ring_share_literal
+_orig_closed = orc.visible_pairs_closed_form
+
+
+def _mut_merge_no_rescale(p1, p2):
+    m1, l1, a1 = p1
+    m2, l2, a2 = p2
+    return np.maximum(m1, m2), l1 + l2, a1 + a2
+
+
+def _mut_merge_wrong_sign(p1, p2):
+    m1, l1, a1 = p1
+    m2, l2, a2 = p2
+    m = np.maximum(m1, m2)
+    f1 = np.where(np.isfinite(m1), np.exp(np.where(np.isfinite(m1), m - m1, 0.0)), 0.0)
+    f2 = np.where(np.isfinite(m2), np.exp(np.where(np.isfinite(m2), m - m2, 0.0)), 0.0)
+    return m, f1 * l1 + f2 * l2, f1[..., None] * a1 + f2[..., None] * a2
+
+
+def _mut_merge_acc_unscaled(p1, p2):
+    m, l, _ = _orig_merge(p1, p2)
+    return m, l, p1[2] + p2[2]
+
+
+def _mut_visibility_strict(q_pos, k_pos, causal):
+    if not causal:
+        return np.ones((q_pos.size, k_pos.size), dtype=bool)
+    return k_pos[None, :] < q_pos[:, None]
+
+
+def _mut_visibility_transposed(q_pos, k_pos, causal):
+    if not causal:
+        return np.ones((q_pos.size, k_pos.size), dtype=bool)
+    return k_pos[None, :] >= q_pos[:, None]
+
+
+def _mut_block_partial_transposed_v(q, q_pos, k, v, k_pos, causal, scale=None):
+    m, l, acc = _orig_block_partial(q, q_pos, k, v, k_pos, causal, scale)
+    return m, l, acc[:, ::-1]
+
+
+def _mut_finalize_no_divide(state):
+    m, l, acc = state
+    return acc, m + np.log(np.where(l > 0, l, 1.0))
+
+
+def _mut_literal_no_scale(q_share, k_blocks, v_blocks, rank, n_ring, scale=None):
+    return _orig_literal(q_share, k_blocks, v_blocks, rank, n_ring, scale=1.0)
+
+
+def _mut_closed_form(layout, causal, n_ring, rank, block_len):
+    if causal and layout == "striped":
+        return n_ring * block_len * (block_len - 1) // 2 + rank * block_len
+    return _orig_closed(layout, causal, n_ring, rank, block_len)
+
+
+def _mut_ring_order(rank, n_ring):
+    return [(rank + s) % n_ring for s in range(n_ring - 1)]  # drops the last block
+
+
+MUTANTS = {
+    "gqa_head_map": ("kv_head_of", _mut_kv_head),
+    "scale_1_over_d": ("default_scale", _mut_scale),
+    "striped_positions": ("global_positions", _mut_positions_striped),
+    "contiguous_off_by_one": ("global_positions", _mut_positions_contiguous_off_by_one),
+    "merge_no_rescale": ("merge_partials", _mut_merge_no_rescale),
+    "merge_wrong_sign": ("merge_partials", _mut_merge_wrong_sign),
+    "merge_acc_unscaled": ("merge_partials", _mut_merge_acc_unscaled),
+    "causal_excludes_self": ("_visibility", _mut_visibility_strict),
+    "causal_mask_transposed": ("_visibility", _mut_visibility_transposed),
+    "acc_rows_permuted": ("block_partial", _mut_block_partial_transposed_v),
+    "finalize_no_divide": ("finalize", _mut_finalize_no_divide),
+    "literal_no_scale": ("ring_share_literal", _mut_literal_no_scale),
+    "striped_pair_count": ("visible_pairs_closed_form", _mut_closed_form),
+    "ring_order_drops_block": ("ring_order", _mut_ring_order),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    with np.errstate(all="ignore"):
+        assert not _pins_hold(), f"mutant {name} survived the pins"

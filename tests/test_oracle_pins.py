@@ -1,0 +1,397 @@
+"""Pins for the CPU oracle: what the pages and plain mathematics fix.
+
+Each test checks the oracle against something other than itself: the worked
+example printed on the Ultralytics "Ring Attention" page, torch's CPU
+scaled_dot_product_attention in float64 (a library routine written
+independently of the oracle), pure-Python brute force on tiny inputs, closed
+forms and invariants.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ring_oracle as orc
+from ring_attention_blockwise_ra_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LAYOUTS = ("contiguous", "striped")
+
+
+def _np(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def _blocks_from_global(x, layout, n_ring):
+    """[B, S, H, d] global -> [N, B, S/N, H, d] by an explicit per-token loop
+    (independent of the oracle's position helper)."""
+    bsz, seq, h, d = x.shape
+    blen = seq // n_ring
+    out = np.empty((n_ring, bsz, blen, h, d))
+    for t in range(seq):
+        if layout == "contiguous":
+            j, a = t // blen, t % blen
+        else:
+            j, a = t % n_ring, t // n_ring
+        out[j, :, a] = x[:, t]
+    return out
+
+
+def _share_rows(layout, n_ring, rank, blen):
+    """Global token index of each local query row, by explicit enumeration."""
+    rows = []
+    for t in range(n_ring * blen):
+        j = t // blen if layout == "contiguous" else t % n_ring
+        if j == rank:
+            rows.append(t)
+    return np.array(rows)
+
+
+def _sdpa64(q, k, v, causal, scale=None):
+    """torch CPU SDPA in float64 on [B, S, H, d] arrays -> [B, S, Hq, d]."""
+    tq = torch.from_numpy(np.ascontiguousarray(q)).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.ascontiguousarray(k)).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(np.ascontiguousarray(v)).permute(0, 2, 1, 3)
+    gqa = tq.shape[1] != tk.shape[1]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=gqa)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def _rand(seed, bsz, seq, hq, hkv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((bsz, seq, hq, d)), rng.standard_normal((bsz, seq, hkv, d)),
+            rng.standard_normal((bsz, seq, hkv, d)))
+
+
+# ---------------------------------------------------------------- P-1 --------
+def test_ultralytics_worked_example():
+    """The page's four-device simulation: blockwise ring equals full
+    attention (allclose, atol 1e-5), each device holding an 8x8 score block
+    while the full matrix is 32x32."""
+    with open(os.path.join(GOLDEN, "ul_four_device_simulation.json")) as f:
+        gold = json.load(f)
+    q, k, v = (_np(t) for t in synth.c1_qkv())
+    n, blen = gold["n_devices"], gold["block"]
+    assert q.shape == (1, n * blen, 1, gold["dim"])
+    kb, vb = _blocks_from_global(k, "contiguous", n), _blocks_from_global(v, "contiguous", n)
+    ring = np.concatenate([orc.ring_share(q[:, i * blen:(i + 1) * blen], kb, vb, i, n,
+                                          "contiguous", False)[0] for i in range(n)], axis=1)
+    literal = np.concatenate([orc.ring_share_literal(q[:, i * blen:(i + 1) * blen], kb, vb, i, n)
+                              for i in range(n)], axis=1)
+    full, _ = orc.naive_attention(q, k, v, causal=False)
+    # library reference of the page's own "full" line: softmax(q k^T / sqrt(dim)) v
+    tq, tk, tv = (torch.from_numpy(x[0, :, 0, :]) for x in (q, k, v))
+    lib = (torch.softmax(tq @ tk.T / gold["dim"] ** 0.5, dim=-1) @ tv).numpy()[None, :, None, :]
+    ok = torch.allclose(torch.from_numpy(ring), torch.from_numpy(lib),
+                        atol=gold["allclose_atol"], rtol=gold["allclose_rtol"])
+    assert ok == gold["matches_full_attention"]
+    assert torch.allclose(torch.from_numpy(literal), torch.from_numpy(lib),
+                          atol=gold["allclose_atol"], rtol=gold["allclose_rtol"])
+    np.testing.assert_allclose(full, lib, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(ring, full, atol=1e-13, rtol=0)
+    # score block held by one device vs the full score matrix
+    assert [blen, kb.shape[2]] == gold["largest_score_block_per_device"]
+    assert [q.shape[1], k.shape[1]] == gold["full_matrix"]
+
+
+# ---------------------------------------------------------------- P-2 --------
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 2), (6, 3)])
+def test_causal_row0_is_v0(layout, hq, hkv):
+    n, blen, d = 4, 6, 8
+    q, k, v = _rand(11, 2, n * blen, hq, hkv, d)
+    out, _ = orc.naive_attention(q, k, v, causal=True)
+    kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+    rows = _share_rows(layout, n, 0, blen)
+    assert rows[0] == 0
+    o2, _ = orc.ring_share(q[:, rows], kb, vb, 0, n, layout, True)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        np.testing.assert_array_equal(out[:, 0, h], v[:, 0, g])
+        np.testing.assert_allclose(o2[:, 0, h], v[:, 0, g], atol=1e-15, rtol=0)
+
+
+# ---------------------------------------------------------------- P-3 --------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_constant_keys_give_mean_of_visible_values(causal, layout):
+    n, blen, d, hq, hkv = 3, 5, 4, 2, 1
+    q, _, v = _rand(5, 1, n * blen, hq, hkv, d)
+    k = np.broadcast_to(np.linspace(-1, 1, d), (1, n * blen, hkv, d)).copy()
+    out, _ = orc.naive_attention(q, k, v, causal)
+    for t in range(n * blen):
+        want = v[:, : t + 1, 0].mean(axis=1) if causal else v[:, :, 0].mean(axis=1)
+        for h in range(hq):
+            np.testing.assert_allclose(out[:, t, h], want, atol=1e-13, rtol=0)
+    kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+    for r in range(n):
+        rows = _share_rows(layout, n, r, blen)
+        o2, _ = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal)
+        np.testing.assert_allclose(o2, out[:, rows], atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- P-4 --------
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_arrival_order_invariance(layout, causal):
+    n, blen, d = 5, 4, 8
+    q, k, v = _rand(3, 1, n * blen, 4, 2, d)
+    q = q * 3.0  # widen the score range so rescaling matters
+    kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+    rng = np.random.default_rng(0)
+    for r in range(n):
+        rows = _share_rows(layout, n, r, blen)
+        base, lse0 = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal)
+        for _ in range(4):
+            perm = list(rng.permutation(n))
+            o, lse = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal, order=perm)
+            np.testing.assert_allclose(o, base, atol=1e-13, rtol=0)
+            np.testing.assert_allclose(lse, lse0, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- P-5/P-6 ----
+_TINY = list(itertools.product([1, 2, 3, 4], [1, 2, 3, 5, 8], [(1, 1), (2, 1), (4, 2)], LAYOUTS,
+                               [False, True]))
+
+
+@pytest.mark.parametrize("n,blen,heads,layout,causal", _TINY)
+def test_brute_force_tiny_vs_sdpa(n, blen, heads, layout, causal):
+    hq, hkv = heads
+    d = 16
+    q, k, v = _rand(n * 100 + blen, 1, n * blen, hq, hkv, d)
+    ref = _sdpa64(q, k, v, causal)
+    out, _ = orc.naive_attention(q, k, v, causal)
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+    kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+    for r in range(n):
+        rows = _share_rows(layout, n, r, blen)
+        o2, _ = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal)
+        np.testing.assert_allclose(o2, ref[:, rows], atol=1e-12, rtol=0)
+
+
+def test_pure_python_brute_force():
+    """Scalar loops with math.exp: no matmul, no vectorised softmax."""
+    n, blen, d, hq, hkv = 3, 2, 3, 2, 1
+    q, k, v = _rand(9, 1, n * blen, hq, hkv, d)
+    scale = 1 / math.sqrt(d)
+    for layout, causal in itertools.product(LAYOUTS, [False, True]):
+        kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+        for r in range(n):
+            rows = _share_rows(layout, n, r, blen)
+            o2, _ = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal)
+            for a, t in enumerate(rows):
+                for h in range(hq):
+                    w = []
+                    for u in range(n * blen):
+                        if causal and u > t:
+                            continue
+                        s = sum(q[0, t, h, i] * k[0, u, 0, i] for i in range(d)) * scale
+                        w.append((u, math.exp(s)))
+                    z = sum(e for _, e in w)
+                    for i in range(d):
+                        want = sum(e * v[0, u, 0, i] for u, e in w) / z
+                        assert abs(o2[0, a, h, i] - want) < 1e-13
+
+
+def test_single_block_ring_is_plain_attention():
+    q, k, v = _rand(4, 2, 7, 4, 4, 16)
+    for causal in (False, True):
+        o2, _ = orc.ring_share(q, k[None], v[None], 0, 1, "contiguous", causal)
+        np.testing.assert_allclose(o2, _sdpa64(q, k, v, causal), atol=1e-12, rtol=0)
+
+
+def test_lse_matches_library_logsumexp():
+    q, k, v = _rand(8, 1, 12, 2, 1, 8)
+    out, lse = orc.naive_attention(q, k, v, causal=True)
+    s = torch.from_numpy(q[0, :, 1] @ k[0, :, 0].T / math.sqrt(8))
+    s = s.masked_fill(torch.triu(torch.ones(12, 12, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(lse[0, :, 1], torch.logsumexp(s, dim=-1).numpy(), atol=1e-13, rtol=0)
+    kb, vb = _blocks_from_global(k, "striped", 3), _blocks_from_global(v, "striped", 3)
+    rows = _share_rows("striped", 3, 2, 4)
+    _, lse2 = orc.ring_share(q[:, rows], kb, vb, 2, 3, "striped", True)
+    np.testing.assert_allclose(lse2, lse[:, rows], atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- P-7 --------
+def test_affine_values():
+    q, k, v = _rand(21, 1, 12, 2, 2, 8)
+    alpha, beta = -1.7, 0.3
+    for causal in (False, True):
+        o, _ = orc.naive_attention(q, k, v, causal)
+        o_aff, _ = orc.naive_attention(q, k, alpha * v + beta, causal)
+        np.testing.assert_allclose(o_aff, alpha * o + beta, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- P-8 --------
+def _rand_partial(rng, shape, d, empty_rows=()):
+    m = rng.standard_normal(shape) * 3
+    l = rng.uniform(1, 10, shape)
+    acc = rng.standard_normal(shape + (d,))
+    for idx in empty_rows:
+        m[idx], l[idx], acc[idx] = -np.inf, 0.0, 0.0
+    return m, l, acc
+
+
+def test_merge_algebra():
+    rng = np.random.default_rng(1)
+    shape, d = (2, 5, 3), 4
+    x = _rand_partial(rng, shape, d, empty_rows=[(0, 1, 2)])
+    y = _rand_partial(rng, shape, d, empty_rows=[(0, 1, 2), (1, 0, 0)])
+    z = _rand_partial(rng, shape, d)
+    e = orc.empty_partial(2, 5, 3, d)
+    # identity
+    for a, b in zip(orc.merge_partials(x, e), x):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(orc.merge_partials(e, x), x):
+        np.testing.assert_array_equal(a, b)
+    # empty with empty stays empty, no NaN
+    m, l, acc = orc.merge_partials(e, e)
+    assert np.all(m == -np.inf) and np.all(l == 0) and np.all(acc == 0)
+    # merge(x, x) = (m, 2l, 2acc)
+    m, l, acc = orc.merge_partials(x, x)
+    np.testing.assert_array_equal(m, x[0])
+    np.testing.assert_allclose(l, 2 * x[1], rtol=1e-15)
+    np.testing.assert_allclose(acc, 2 * x[2], rtol=1e-15)
+    # commutative and associative
+    for a, b in zip(orc.merge_partials(x, y), orc.merge_partials(y, x)):
+        np.testing.assert_allclose(a, b, rtol=1e-15, atol=0)
+    lhs = orc.merge_partials(orc.merge_partials(x, y), z)
+    rhs = orc.merge_partials(x, orc.merge_partials(y, z))
+    for a, b in zip(lhs, rhs):
+        np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-300)
+    # merged result: m is the max, l and acc are the rescaled sums (direct formula)
+    m, l, acc = orc.merge_partials(x, z)
+    np.testing.assert_array_equal(m, np.maximum(x[0], z[0]))
+    wx = np.where(np.isfinite(x[0]), np.exp(np.where(np.isfinite(x[0]), x[0], 0) - m), 0)
+    np.testing.assert_allclose(l, wx * x[1] + np.exp(z[0] - m) * z[1], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- P-9 --------
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_partial_statistics(layout):
+    n, blen, d, hq, hkv = 4, 5, 8, 2, 1
+    q, k, v = _rand(31, 1, n * blen, hq, hkv, d)
+    scale = 1 / math.sqrt(d)
+    kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+    for r, j in itertools.product(range(n), range(n)):
+        rows = _share_rows(layout, n, r, blen)
+        keys = _share_rows(layout, n, j, blen)
+        m, l, acc = orc.block_partial(q[:, rows], rows, kb[j], vb[j], keys, True, scale)
+        for a, t in enumerate(rows):
+            vis = [b for b, u in enumerate(keys) if u <= t]
+            for h in range(hq):
+                if not vis:
+                    assert m[0, a, h] == -np.inf and l[0, a, h] == 0 and np.all(acc[0, a, h] == 0)
+                    continue
+                scores = [float(np.dot(q[0, t, h], kb[j, 0, b, 0])) * scale for b in vis]
+                assert abs(m[0, a, h] - max(scores)) < 1e-13
+                assert 1.0 - 1e-15 <= l[0, a, h] <= len(vis) + 1e-12
+
+
+# ---------------------------------------------------------------- P-10 -------
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_split_ring_checkpoint(layout):
+    n, blen = 6, 4
+    q, k, v = _rand(41, 1, n * blen, 2, 2, 8)
+    kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+    for r in range(n):
+        rows = _share_rows(layout, n, r, blen)
+        order = orc.ring_order(r, n)
+        whole = orc.ring_state(q[:, rows], kb, vb, r, n, layout, True)
+        for cut in range(n + 1):
+            first = orc.ring_state(q[:, rows], kb, vb, r, n, layout, True, blocks=order[:cut])
+            rest = orc.ring_state(q[:, rows], kb, vb, r, n, layout, True, blocks=order[cut:])
+            both = orc.merge_partials(first, rest)
+            for a, b in zip(orc.finalize(both), orc.finalize(whole)):
+                np.testing.assert_allclose(a, b, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- positions --
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_positions_partition_the_sequence(layout):
+    for n, blen in [(1, 5), (3, 4), (8, 16)]:
+        allpos = np.concatenate([orc.global_positions(layout, n, j, blen) for j in range(n)])
+        assert sorted(allpos.tolist()) == list(range(n * blen))
+        for j in range(n):
+            np.testing.assert_array_equal(orc.global_positions(layout, n, j, blen),
+                                          _share_rows(layout, n, j, blen))
+
+
+def test_ring_order_visits_every_block_once_starting_local():
+    for n in range(1, 9):
+        for r in range(n):
+            order = orc.ring_order(r, n)
+            assert order[0] == r and sorted(order) == list(range(n))
+            # step s uses the block that arrived from the previous device
+            for s in range(1, n):
+                assert order[s] == (order[s - 1] - 1) % n
+
+
+# ---------------------------------------------------------------- P-11 -------
+def test_tile_classes_hand_example():
+    # contiguous, 4 tokens per block, 2x2 tiles, diagonal block: lower
+    # triangle -> FULL below the diagonal, PARTIAL on it, SKIP above.
+    c = orc.tile_classes_bruteforce("contiguous", True, 2, 1, 1, 4, 4, 2, 2)
+    np.testing.assert_array_equal(c, [[orc.PARTIAL, orc.SKIP], [orc.FULL, orc.PARTIAL]])
+    assert np.all(orc.tile_classes_bruteforce("contiguous", True, 2, 1, 0, 4, 4, 2, 2) == orc.FULL)
+    assert np.all(orc.tile_classes_bruteforce("contiguous", True, 2, 0, 1, 4, 4, 2, 2) == orc.SKIP)
+    # striped, block j > r loses the diagonal: 1x1 tiles have no PARTIAL
+    c = orc.tile_classes_bruteforce("striped", True, 4, 1, 2, 3, 3, 1, 1)
+    np.testing.assert_array_equal(c, [[0, 0, 0], [2, 0, 0], [2, 2, 0]])
+    c = orc.tile_classes_bruteforce("striped", True, 4, 2, 1, 3, 3, 1, 1)
+    np.testing.assert_array_equal(c, [[2, 0, 0], [2, 2, 0], [2, 2, 2]])
+    assert np.all(orc.tile_classes_bruteforce("striped", False, 4, 2, 1, 5, 5, 2, 3) == orc.FULL)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_tile_counts_closed_form_vs_bruteforce(layout):
+    sizes = [1, 2, 4, 8, 16]
+    for n, blen in [(2, 8), (3, 13), (4, 16), (8, 9)]:
+        for tq, tk in itertools.product(sizes, sizes):
+            if tq == tk and tq not in (1, 8):
+                continue
+            for r, j in itertools.product(range(n), range(n)):
+                for causal in (True, False):
+                    c = orc.tile_classes_bruteforce(layout, causal, n, r, j, blen, blen, tq, tk)
+                    want = (int((c == orc.FULL).sum()), int((c == orc.PARTIAL).sum()),
+                            int((c == orc.SKIP).sum()))
+                    got = orc.tile_class_counts(layout, causal, n, r, j, blen, blen, tq, tk)
+                    assert got == want, (layout, n, blen, tq, tk, r, j, causal)
+
+
+def test_tile_counts_real_size_closed_form():
+    """At the 1M-token share (B=131072, 128x128 tiles), a diagonal-type block
+    has nt(nt-1)/2 FULL, nt PARTIAL, nt(nt-1)/2 SKIP tiles (nt = 1024)."""
+    nt = 1024
+    for layout, r, j in [("contiguous", 7, 7), ("striped", 7, 3), ("striped", 3, 7)]:
+        got = orc.tile_class_counts(layout, True, 8, r, j, 131072, 131072, 128, 128)
+        assert got == (nt * (nt - 1) // 2, nt, nt * (nt - 1) // 2)
+    assert orc.tile_class_counts("contiguous", True, 8, 7, 2, 131072, 131072, 128, 128) == (nt * nt, 0, 0)
+    assert orc.tile_class_counts("contiguous", True, 8, 2, 7, 131072, 131072, 128, 128) == (0, 0, nt * nt)
+
+
+# ---------------------------------------------------------------- P-12 -------
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_visible_pair_closed_forms(layout):
+    for n, blen in [(4, 8), (8, 16), (3, 5), (1, 7), (5, 1)]:
+        for r in range(n):
+            for causal in (True, False):
+                assert (orc.visible_pairs_closed_form(layout, causal, n, r, blen)
+                        == orc.visible_pairs_bruteforce(layout, causal, n, r, blen))
+
+
+def test_counted_flops_at_real_sizes():
+    # contiguous r=7: 7 B^2 + B(B+1)/2 pairs; striped r=7: 8 B(B-1)/2 + 8 B
+    b = 131072
+    pc = orc.visible_pairs_closed_form("contiguous", True, 8, 7, b)
+    ps = orc.visible_pairs_closed_form("striped", True, 8, 7, b)
+    assert pc == 128_849_084_416 and ps == 68_720_001_024
+    assert orc.counted_flops(pc, 128, 32) == 16384 * 128_849_084_416
+    assert orc.counted_flops(orc.visible_pairs_closed_form("contiguous", False, 8, 0, 115200), 128, 32) \
+        == 4 * 128 * 32 * 8 * 115200 ** 2
