@@ -1,0 +1,187 @@
+/*
+ * ra.h -- C ABI of the MI355X (gfx950) Ring Attention per-device library.
+ *
+ * One device's share of Ring Attention: a fixed local query block attends to
+ * N arriving key/value blocks; each block yields a partial (running max m,
+ * normaliser l, unnormalised accumulator acc) and partials are merged by
+ * online-softmax rescaling. On one GPU the ring is a loop of N steps whose
+ * next block is staged by a double-buffered device-to-device copy on a side
+ * stream.
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [UL] Ultralytics glossary "Ring Attention", section "How ring attention
+ *        works": N blocks, each device keeps its query block, attends to the
+ *        block it holds, forwards it and receives the next; running sums of
+ *        exponentiated scores and of weighted values, divided at the end;
+ *        max subtraction in production kernels; striped token assignment.
+ *   [TS] troisinh.com "Ring Attention -- K/V truyen vong giua GPU, context
+ *        trieu token", sections "Y tuong cot loi" (fixed Q, K/V rotating,
+ *        associative merge) and "Tai sao no hoat dong" (the running max and
+ *        normaliser update; output rescaled the same way).
+ *   [JS] jisaku.com glossary "Ring Attention", sections on the processing
+ *        flow and on overlapping communication with computation.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are row-major [batch, seq, heads, head_dim], head_dim
+ *     contiguous. Query head h reads KV head h / (hq / hkv).
+ *   - q, k, v are bfloat16 (RA_BF16) or float32 (RA_F32); m, l, acc, out,
+ *     lse are float32. m is in natural-log units of scaled scores.
+ *   - All pointers are device pointers the caller allocated; the library
+ *     never allocates or frees device memory. Every data pointer must be
+ *     16-byte aligned. Streams are hipStream_t passed as void* (NULL = the
+ *     null stream of the current device); the current HIP device must be the
+ *     device owning the pointers and streams.
+ *   - Validation runs on the host before any HIP call. On failure an entry
+ *     point returns a non-zero ra_status, sets ra_last_error(), and enqueues
+ *     nothing. HIP API failures return RA_ERR_HIP. Work is asynchronous:
+ *     device faults surface at the caller's next synchronisation. No C++
+ *     exception crosses this ABI.
+ *   - Empty problems (batch, q_len or hq*... zero) return RA_OK and enqueue
+ *     nothing.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1,  /* bad shape, pointer, alignment, enum, alias   */
+  RA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim)         */
+  RA_ERR_WORKSPACE = 3,    /* workspace missing or too small               */
+  RA_ERR_HIP = 4           /* a HIP runtime call or launch failed          */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* Token layouts ([UL] striping remark; contiguous chunks per device).
+ * contiguous: block i holds global tokens [i*B, (i+1)*B).
+ * striped:    token t belongs to block t mod N at local index t / N.
+ * The caller stores q, k, v already in the layout's token order. */
+typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1 } ra_layout;
+
+/* Class of a (query tile, key tile) pair under the causal mask. */
+typedef enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 } ra_tile_class;
+
+typedef struct {
+  int32_t dtype;     /* ra_dtype of q, k, v                                  */
+  int32_t batch;     /* >= 0                                                 */
+  int32_t hq;        /* query heads, >= 1                                    */
+  int32_t hkv;       /* key/value heads, >= 1, hq % hkv == 0                 */
+  int32_t head_dim;  /* 16, 32, 64 or 128 (others: RA_ERR_UNSUPPORTED)       */
+  int64_t q_len;     /* local queries (this device's block), 0..2^30         */
+  int64_t kv_len;    /* keys per KV block, 0..2^30                           */
+  int32_t n_ring;    /* N >= 1                                               */
+  int32_t rank;      /* r, 0 <= r < N: the device whose share is computed    */
+  int32_t causal;    /* 0 or 1; causal requires q_len == kv_len              */
+  int32_t layout;    /* ra_layout                                            */
+  float scale;       /* score scale; <= 0 selects 1/sqrt(head_dim); NaN/inf
+                        are invalid                                          */
+} ra_problem;
+
+/*
+ * Partial attention of the local queries against one arriving KV block j
+ * ([UL] "How ring attention works": the per-step computation against the
+ * block the device currently holds; max subtraction as in production kernels).
+ *
+ *   q   [batch, q_len, hq, head_dim]   dtype, read
+ *   k,v [batch, kv_len, hkv, head_dim] dtype, read: block j's tokens
+ *   m,l [batch, q_len, hq]             float32, written
+ *   acc [batch, q_len, hq, head_dim]   float32, written
+ * For each query row: m = max visible scaled score, l = sum exp(s - m),
+ * acc = sum exp(s - m) v. Rows with no visible key get (-inf, 0, 0). Global
+ * positions come from (layout, n_ring, rank) for queries and (layout,
+ * n_ring, j) for keys; causal masks keys whose position exceeds the query's.
+ * Fully masked (query tile, key tile) pairs are never computed.
+ * Outputs must not overlap the inputs.
+ */
+ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j,
+                                const void* q, const void* k, const void* v,
+                                float* m, float* l, float* acc, void* hip_stream);
+
+/*
+ * Online-softmax merge of two partials ([TS] "Tai sao no hoat dong"):
+ *   m = max(m1, m2); a_i = exp(m_i - m) (0 when m_i = -inf);
+ *   l = a1 l1 + a2 l2; acc = a1 acc1 + a2 acc2.
+ * Two empty partials merge to (-inf, 0, 0). rows = batch*q_len*hq;
+ * m*, l* are [rows] and acc* [rows, head_dim], float32. The outputs may alias
+ * input 1 or input 2 exactly (in-place running update), not partially.
+ */
+ra_status ra_merge_partials(int64_t rows, int32_t head_dim,
+                            const float* m1, const float* l1, const float* acc1,
+                            const float* m2, const float* l2, const float* acc2,
+                            float* m_out, float* l_out, float* acc_out,
+                            void* hip_stream);
+
+/*
+ * Final divide ([UL]: the accumulated numerator is divided by the
+ * denominator at the end): acc <- acc / l in place, and, when lse is not
+ * NULL, lse = m + ln l. Rows with l == 0 give 0 and lse = -inf.
+ */
+ra_status ra_finalize(int64_t rows, int32_t head_dim, const float* m, const float* l,
+                      float* acc, float* lse, void* hip_stream);
+
+/* Workspace bytes ra_ring_fwd needs for this problem (0 on invalid input):
+ * two staging buffers for K and two for V, one partial (m, l, acc) and the
+ * running m and l. */
+size_t ra_ring_workspace_bytes(const ra_problem* prob);
+
+/*
+ * One device's whole share of the ring ([UL] "How ring attention works";
+ * [JS] processing flow and communication/compute overlap).
+ *
+ *   q     [batch, q_len, hq, head_dim]            dtype: local queries
+ *   k, v  [n_ring, batch, kv_len, hkv, head_dim]  dtype: all N blocks,
+ *         stored in the layout's token order (a stand-in for the blocks that
+ *         would arrive from the previous device)
+ *   out   [batch, q_len, hq, head_dim] float32: attention output; also used
+ *         as the running accumulator
+ *   lse   [batch, q_len, hq] float32 or NULL: m + ln l
+ *   workspace: device buffer of at least ra_ring_workspace_bytes(prob)
+ *
+ * Step s uses block j = (rank - s) mod N. Step 0 reads the local block in
+ * place; for s >= 1 block j is first copied into staging buffer s % 2 on
+ * copy_stream while step s-1 computes on compute_stream (events order the
+ * copy after the last read of that buffer, and the compute after the copy).
+ * Blocks whose every pair is masked are still staged but not computed.
+ * copy_stream may be NULL or equal to compute_stream: copies then run in
+ * order on compute_stream. On return all work is enqueued; everything
+ * enqueued on copy_stream is ordered before the last kernel on
+ * compute_stream, so synchronising compute_stream is enough.
+ * Calls on the same device are serialised internally while enqueuing;
+ * concurrent calls must not share a workspace.
+ */
+ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, const void* v,
+                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream);
+
+/*
+ * Causal tile scheduler, host mirror. Class of the pair (query rows
+ * [a_lo, a_hi], keys [b_lo, b_hi]) of block j (local indices, inclusive).
+ * Returns an ra_tile_class, or -1 on invalid input. The attention kernels
+ * decide which tiles to visit and which to mask with the same rule.
+ */
+int32_t ra_tile_class_host(const ra_problem* prob, int32_t kv_block_j,
+                           int64_t a_lo, int64_t a_hi, int64_t b_lo, int64_t b_hi);
+
+/* Classes of the full grid of tq x tk tiles of block j, row-major
+ * [ceil(q_len/tq), ceil(kv_len/tk)] int8, into host memory (host mirror) or
+ * device memory (computed by a kernel with the device form of the rule). */
+ra_status ra_tile_classes_host(const ra_problem* prob, int32_t kv_block_j, int32_t tq,
+                               int32_t tk, int8_t* out_host);
+ra_status ra_tile_classes_device(const ra_problem* prob, int32_t kv_block_j, int32_t tq,
+                                 int32_t tk, int8_t* out_device, void* hip_stream);
+
+/* Thread-local message describing the last failure on this thread. */
+const char* ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

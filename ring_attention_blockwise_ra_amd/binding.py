@@ -1,0 +1,290 @@
+"""Thin ctypes binding of the C ABI in include/ra.h (argument marshalling only).
+
+Every function here checks tensor shapes, dtypes and devices, allocates
+outputs with torch when the caller did not pass them, and calls the HIP
+library with raw device pointers and the current HIP stream. No step of the
+attention path runs in Python. If the built library is missing, every call
+raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libra_amd.so")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(5)
+RA_F32, RA_BF16 = 0, 1
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
+RA_TILE_SKIP, RA_TILE_PARTIAL, RA_TILE_FULL = 0, 1, 2
+
+_LAYOUT = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED,
+           RA_LAYOUT_CONTIGUOUS: RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED: RA_LAYOUT_STRIPED}
+_DTYPE = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
+
+EXPORTED = (
+    "ra_block_attn_partial", "ra_merge_partials", "ra_finalize", "ra_ring_workspace_bytes",
+    "ra_ring_fwd", "ra_tile_class_host", "ra_tile_classes_host", "ra_tile_classes_device",
+    "ra_last_error",
+)
+
+
+class RaProblem(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("hq", ctypes.c_int32),
+        ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int64),
+        ("kv_len", ctypes.c_int64), ("n_ring", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("layout", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
+class RaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ra status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libra_amd.so (built by ring_attention_blockwise_ra_amd.build)."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"HIP library not built: {LIB_PATH} is missing "
+                    "(run python -m ring_attention_blockwise_ra_amd.build)")
+            L = ctypes.CDLL(LIB_PATH)
+            P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+            PP = ctypes.POINTER(RaProblem)
+            L.ra_block_attn_partial.argtypes = [PP, I32, P, P, P, P, P, P, P]
+            L.ra_block_attn_partial.restype = I32
+            L.ra_merge_partials.argtypes = [I64, I32, P, P, P, P, P, P, P, P, P, P]
+            L.ra_merge_partials.restype = I32
+            L.ra_finalize.argtypes = [I64, I32, P, P, P, P, P]
+            L.ra_finalize.restype = I32
+            L.ra_ring_workspace_bytes.argtypes = [PP]
+            L.ra_ring_workspace_bytes.restype = ctypes.c_size_t
+            L.ra_ring_fwd.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P, P]
+            L.ra_ring_fwd.restype = I32
+            L.ra_tile_class_host.argtypes = [PP, I32, I64, I64, I64, I64]
+            L.ra_tile_class_host.restype = I32
+            L.ra_tile_classes_host.argtypes = [PP, I32, I32, I32, P]
+            L.ra_tile_classes_host.restype = I32
+            L.ra_tile_classes_device.argtypes = [PP, I32, I32, I32, P, P]
+            L.ra_tile_classes_device.restype = I32
+            L.ra_last_error.argtypes = []
+            L.ra_last_error.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != RA_OK:
+        raise RaError(status, lib().ra_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(None if t is None else t.data_ptr())
+
+
+def _stream(s, device) -> ctypes.c_void_p:
+    if s is None:
+        s = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_problem(*, dtype, batch, hq, hkv, head_dim, q_len, kv_len, n_ring, rank, causal,
+                 layout, scale=None) -> RaProblem:
+    return RaProblem(
+        dtype=_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+        batch=int(batch), hq=int(hq), hkv=int(hkv), head_dim=int(head_dim),
+        q_len=int(q_len), kv_len=int(kv_len), n_ring=int(n_ring), rank=int(rank),
+        causal=int(bool(causal)), layout=_LAYOUT[layout],
+        scale=float(scale) if scale is not None else 0.0)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _qkv_problem(q, k, n_ring, rank, causal, layout, scale):
+    if q.dim() != 4 or k.dim() < 4:
+        raise ValueError("q must be [batch, q_len, hq, d]; k, v [.., batch, kv_len, hkv, d]")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[-3], k.shape[-2]
+    return make_problem(dtype=q.dtype, batch=b, hq=hq, hkv=hkv, head_dim=d, q_len=lq, kv_len=lk,
+                        n_ring=n_ring, rank=rank, causal=causal, layout=layout, scale=scale)
+
+
+def ra_block_attn_partial(q, k, v, kv_block_j: int, *, n_ring: int, rank: int, causal: bool,
+                          layout="contiguous", scale=None, m=None, l=None, acc=None, stream=None):
+    """Partial (m, l, acc) of q against KV block kv_block_j (see include/ra.h)."""
+    _need(q, "q")
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale)
+    b, lq, hq, d = q.shape
+    _need(k, "k", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
+    _need(v, "v", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
+    m = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device) if m is None else m
+    l = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device) if l is None else l
+    acc = torch.empty(b, lq, hq, d, dtype=torch.float32, device=q.device) if acc is None else acc
+    _need(m, "m", torch.float32, (b, lq, hq), q.device)
+    _need(l, "l", torch.float32, (b, lq, hq), q.device)
+    _need(acc, "acc", torch.float32, (b, lq, hq, d), q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().ra_block_attn_partial(ctypes.byref(prob), int(kv_block_j), _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(m), _ptr(l), _ptr(acc),
+                                           _stream(stream, q.device)))
+    return m, l, acc
+
+
+def ra_merge_partials(m1, l1, acc1, m2, l2, acc2, *, out=None, stream=None):
+    """(m1, l1, acc1) merged with (m2, l2, acc2); out=(m, l, acc) may be input 1."""
+    _need(acc1, "acc1", torch.float32)
+    d = acc1.shape[-1]
+    rows = acc1.numel() // d if d else 0
+    dev = acc1.device
+    for name, t in (("m1", m1), ("l1", l1), ("m2", m2), ("l2", l2)):
+        _need(t, name, torch.float32, device=dev)
+        if t.numel() != rows:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {rows}")
+    _need(acc2, "acc2", torch.float32, acc1.shape, dev)
+    if out is None:
+        out = (torch.empty_like(m1), torch.empty_like(l1), torch.empty_like(acc1))
+    mo, lo, ao = out
+    _need(mo, "m_out", torch.float32, m1.shape, dev)
+    _need(lo, "l_out", torch.float32, l1.shape, dev)
+    _need(ao, "acc_out", torch.float32, acc1.shape, dev)
+    with torch.cuda.device(dev):
+        _check(lib().ra_merge_partials(rows, d, _ptr(m1), _ptr(l1), _ptr(acc1), _ptr(m2),
+                                       _ptr(l2), _ptr(acc2), _ptr(mo), _ptr(lo), _ptr(ao),
+                                       _stream(stream, dev)))
+    return mo, lo, ao
+
+
+def ra_finalize(m, l, acc, *, lse=None, want_lse=True, stream=None):
+    """acc <- acc / l in place; returns (acc, lse)."""
+    _need(acc, "acc", torch.float32)
+    d = acc.shape[-1]
+    rows = acc.numel() // d if d else 0
+    dev = acc.device
+    _need(m, "m", torch.float32, device=dev)
+    _need(l, "l", torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty_like(m)
+    with torch.cuda.device(dev):
+        _check(lib().ra_finalize(rows, d, _ptr(m), _ptr(l), _ptr(acc), _ptr(lse),
+                                 _stream(stream, dev)))
+    return acc, lse
+
+
+def ra_ring_workspace_bytes(prob: RaProblem) -> int:
+    return int(lib().ra_ring_workspace_bytes(ctypes.byref(prob)))
+
+
+def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank: int = None,
+                scale=None, out=None, lse=None, want_lse=True, workspace=None,
+                compute_stream=None, copy_stream="auto"):
+    """One device's share: q [b, lq, hq, d]; k, v [n_ring, b, lk, hkv, d].
+
+    Returns (out fp32 [b, lq, hq, d], lse fp32 [b, lq, hq] or None).
+    copy_stream: "auto" (a dedicated side stream per device), None (copies
+    in order on the compute stream) or a torch.cuda.Stream.
+    """
+    if rank is None:
+        rank = n_ring - 1
+    _need(q, "q")
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale)
+    b, lq, hq, d = q.shape
+    dev = q.device
+    _need(k, "k", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
+    _need(v, "v", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
+    out = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "out", torch.float32, (b, lq, hq, d), dev)
+    if lse is None and want_lse:
+        lse = torch.empty(b, lq, hq, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (b, lq, hq), dev)
+    need = ra_ring_workspace_bytes(prob)
+    if need == 0 and b * lq * hq > 0:
+        _check(lib().ra_ring_fwd(ctypes.byref(prob), None, None, None, None, None, None, 0,
+                                 None, None))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        cs = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
+        if copy_stream == "auto":
+            copy_stream = side_stream(dev)
+        xs = ctypes.c_void_p(None) if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+        _check(lib().ra_ring_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _ptr(lse), _ptr(workspace), workspace.numel(),
+                                 ctypes.c_void_p(cs.cuda_stream), xs))
+    return out, lse
+
+
+_side = {}
+
+
+def side_stream(device) -> torch.cuda.Stream:
+    """A default-priority side stream per device for K/V staging copies."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx not in _side:
+        _side[idx] = torch.cuda.Stream(device=idx)
+    return _side[idx]
+
+
+def ra_tile_class_host(prob: RaProblem, kv_block_j: int, a_lo, a_hi, b_lo, b_hi) -> int:
+    c = lib().ra_tile_class_host(ctypes.byref(prob), int(kv_block_j), int(a_lo), int(a_hi),
+                                 int(b_lo), int(b_hi))
+    if c < 0:
+        raise RaError(RA_ERR_INVALID_ARG, lib().ra_last_error().decode())
+    return c
+
+
+def ra_tile_classes_host(prob: RaProblem, kv_block_j: int, tq: int, tk: int) -> np.ndarray:
+    nqt, nkt = -(-prob.q_len // tq), -(-prob.kv_len // tk)
+    out = np.zeros((nqt, nkt), dtype=np.int8)
+    _check(lib().ra_tile_classes_host(ctypes.byref(prob), int(kv_block_j), int(tq), int(tk),
+                                      out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def ra_tile_classes_device(prob: RaProblem, kv_block_j: int, tq: int, tk: int, device="cuda",
+                           stream=None) -> torch.Tensor:
+    nqt, nkt = -(-prob.q_len // tq), -(-prob.kv_len // tk)
+    out = torch.full((nqt, nkt), -1, dtype=torch.int8, device=device)
+    with torch.cuda.device(out.device):
+        _check(lib().ra_tile_classes_device(ctypes.byref(prob), int(kv_block_j), int(tq), int(tk),
+                                            _ptr(out), _stream(stream, out.device)))
+    return out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,543 @@
+// ra_api.hip -- the C ABI of include/ra.h: host-side validation, the causal
+// tile scheduler's host mirror, and the one-GPU ring loop.
+//
+// Ring loop (Ultralytics "Ring Attention", section "How ring attention
+// works"; jisaku "Ring Attention", sections on the processing flow and on
+// overlapping communication with computation): step s uses block
+// j = (rank - s) mod N; while step s computes, the block for step s+1 is
+// brought in. On one GPU "bringing in" is a stream-ordered device-to-device
+// copy on a side stream into one of two staging buffers; events order each
+// copy after the last kernel that read its buffer (write-after-read) and each
+// step's kernels after the copy that filled their buffer (read-after-write).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ra.h"
+#include "ra_kernels.h"
+#include "ra_sched.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ra_status fail(ra_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ra_status hip_fail(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Shape {
+  int64_t rows;        // batch * q_len * hq
+  int64_t q_elems;     // batch * q_len * hq * d
+  int64_t kv_elems;    // batch * kv_len * hkv * d (one block)
+  size_t elem;         // bytes per q/k/v element
+  float scale;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ra_status validate_problem(const ra_problem* p, Shape* s) {
+  if (p == nullptr) return fail(RA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->dtype != RA_F32 && p->dtype != RA_BF16)
+    return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_F32 or RA_BF16", p->dtype);
+  if (p->batch < 0) return fail(RA_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->hq < 1 || p->hkv < 1)
+    return fail(RA_ERR_INVALID_ARG, "hq (%d) and hkv (%d) must be >= 1", p->hq, p->hkv);
+  if (p->hq % p->hkv != 0)
+    return fail(RA_ERR_INVALID_ARG, "hq (%d) is not a multiple of hkv (%d)", p->hq, p->hkv);
+  if (p->head_dim <= 0) return fail(RA_ERR_INVALID_ARG, "head_dim %d <= 0", p->head_dim);
+  if (p->head_dim != 16 && p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (16, 32, 64, 128)", p->head_dim);
+  const int64_t kMaxLen = int64_t(1) << 30;
+  if (p->q_len < 0 || p->q_len > kMaxLen)
+    return fail(RA_ERR_INVALID_ARG, "q_len %lld out of [0, 2^30]", (long long)p->q_len);
+  if (p->kv_len < 0 || p->kv_len > kMaxLen)
+    return fail(RA_ERR_INVALID_ARG, "kv_len %lld out of [0, 2^30]", (long long)p->kv_len);
+  if (p->n_ring < 1) return fail(RA_ERR_INVALID_ARG, "n_ring %d < 1", p->n_ring);
+  if (p->rank < 0 || p->rank >= p->n_ring)
+    return fail(RA_ERR_INVALID_ARG, "rank %d out of [0, n_ring=%d)", p->rank, p->n_ring);
+  if (p->causal != 0 && p->causal != 1)
+    return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", p->causal);
+  if (p->layout != RA_LAYOUT_CONTIGUOUS && p->layout != RA_LAYOUT_STRIPED)
+    return fail(RA_ERR_INVALID_ARG, "layout %d unknown", p->layout);
+  if (p->causal && p->q_len != p->kv_len)
+    return fail(RA_ERR_INVALID_ARG, "causal requires q_len == kv_len (%lld vs %lld)",
+                (long long)p->q_len, (long long)p->kv_len);
+  if (isnan(p->scale) || isinf(p->scale))
+    return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  const int64_t group = p->hq / p->hkv;
+  if (group * p->q_len > INT32_MAX)
+    return fail(RA_ERR_INVALID_ARG, "(hq/hkv)*q_len exceeds 2^31-1");
+  // grid: batch * hkv * ceil(group*q_len/128) workgroups must fit in 2^31
+  const int64_t tiles = (group * p->q_len + 127) / 128;
+  if ((int64_t)p->batch * p->hkv * tiles > INT32_MAX)
+    return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
+  s->rows = (int64_t)p->batch * p->q_len * p->hq;
+  s->q_elems = s->rows * p->head_dim;
+  s->kv_elems = (int64_t)p->batch * p->kv_len * p->hkv * p->head_dim;
+  s->elem = p->dtype == RA_BF16 ? 2 : 4;
+  s->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  return RA_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0 || a == nullptr || b == nullptr) return false;
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+ra_status check_ptr(const void* p, size_t bytes, const char* name) {
+  if (bytes == 0) return RA_OK;
+  if (p == nullptr) return fail(RA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(RA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return RA_OK;
+}
+
+int env_qb() {
+  static int qb = [] {
+    const char* e = getenv("RA_QB");
+    if (e && (e[0] == '1' || e[0] == '2') && e[1] == 0) return e[0] - '0';
+    return 1;
+  }();
+  return qb;
+}
+
+ra::AttnParams make_params(const ra_problem* p, const Shape& s, int32_t j, const void* q,
+                           const void* k, const void* v, float* m, float* l, float* acc) {
+  ra::AttnParams a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.m = m;
+  a.l = l;
+  a.acc = acc;
+  a.q_bstride = p->q_len * p->hq * p->head_dim;
+  a.kv_bstride = p->kv_len * p->hkv * p->head_dim;
+  a.batch = p->batch;
+  a.q_len = (int32_t)p->q_len;
+  a.kv_len = (int32_t)p->kv_len;
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.head_dim = p->head_dim;
+  a.group = p->hq / p->hkv;
+  a.rows_per_bg = (int32_t)(a.group * p->q_len);
+  ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
+  a.geom_kind = g.kind;
+  a.geom_delta = g.delta;
+  a.scale_log2 = s.scale * 1.4426950408889634f;
+  return a;
+}
+
+// Enqueue one block's partial into (m, l, acc). Skipped-block semantics: a
+// block with no visible pair (or no keys) yields the empty partial.
+ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const void* q,
+                          const void* k, const void* v, float* m, float* l, float* acc,
+                          hipStream_t st) {
+  ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
+  hipError_t e;
+  if (g.kind == ra::kNoneVisible || p->kv_len == 0) {
+    e = ra::launch_fill_empty(s.rows, p->head_dim, m, l, acc, st);
+    if (e != hipSuccess) return hip_fail(e, "fill_empty launch");
+    return RA_OK;
+  }
+  ra::AttnParams a = make_params(p, s, j, q, k, v, m, l, acc);
+  e = ra::launch_attention(a, p->dtype == RA_BF16, env_qb(), st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return RA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t stage_k[2], stage_v[2], pm, pl, pacc, rm, rl, total;
+};
+
+WsLayout ws_layout(const ra_problem* p, const Shape& s) {
+  WsLayout w{};
+  const size_t blk = align256((size_t)s.kv_elems * s.elem);
+  const size_t rowb = align256((size_t)s.rows * 4);
+  const size_t accb = align256((size_t)s.q_elems * 4);
+  size_t off = 0;
+  const bool staged = p->n_ring > 1;
+  for (int i = 0; i < 2; ++i) {
+    w.stage_k[i] = off;
+    off += staged ? blk : 0;
+    w.stage_v[i] = off;
+    off += staged ? blk : 0;
+  }
+  w.pm = off; off += rowb;
+  w.pl = off; off += rowb;
+  w.pacc = off; off += staged ? accb : 0;
+  w.rm = off; off += rowb;
+  w.rl = off; off += rowb;
+  w.total = off;
+  return w;
+}
+
+// Per-device event pool for the ring loop (timing disabled).
+struct DeviceEvents {
+  std::mutex mu;
+  bool ready = false;
+  hipEvent_t entry{}, copy_done[2]{}, compute_done[2]{};
+};
+
+std::mutex g_pool_mu;
+std::vector<DeviceEvents*> g_pool;
+
+ra_status get_events(DeviceEvents** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  DeviceEvents* de;
+  {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    if ((int)g_pool.size() <= dev) g_pool.resize(dev + 1, nullptr);
+    if (g_pool[dev] == nullptr) g_pool[dev] = new DeviceEvents();
+    de = g_pool[dev];
+  }
+  *out = de;
+  return RA_OK;
+}
+
+ra_status init_events(DeviceEvents* de) {
+  if (de->ready) return RA_OK;
+  hipEvent_t* all[5] = {&de->entry, &de->copy_done[0], &de->copy_done[1], &de->compute_done[0],
+                        &de->compute_done[1]};
+  for (hipEvent_t* ev : all) {
+    hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  de->ready = true;
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_last_error(void) { return g_err.c_str(); }
+
+ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j, const void* q,
+                                const void* k, const void* v, float* m, float* l, float* acc,
+                                void* hip_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    if (kv_block_j < 0 || kv_block_j >= prob->n_ring)
+      return fail(RA_ERR_INVALID_ARG, "kv_block_j %d out of [0, n_ring=%d)", kv_block_j,
+                  prob->n_ring);
+    const size_t qb = s.q_elems * s.elem, kb = s.kv_elems * s.elem;
+    const size_t rb = s.rows * 4, ab = s.q_elems * 4;
+    if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kb, "k")) ||
+        (st = check_ptr(v, kb, "v")) || (st = check_ptr(m, rb, "m")) ||
+        (st = check_ptr(l, rb, "l")) || (st = check_ptr(acc, ab, "acc")))
+      return st;
+    const void* ins[3] = {q, k, v};
+    const size_t insz[3] = {qb, kb, kb};
+    const void* outs[3] = {m, l, acc};
+    const size_t outsz[3] = {rb, rb, ab};
+    for (int i = 0; i < 3; ++i)
+      for (int o = 0; o < 3; ++o)
+        if (overlap(ins[i], insz[i], outs[o], outsz[o]))
+          return fail(RA_ERR_INVALID_ARG, "outputs must not overlap q, k or v");
+    if (overlap(m, rb, l, rb) || overlap(m, rb, acc, ab) || overlap(l, rb, acc, ab))
+      return fail(RA_ERR_INVALID_ARG, "m, l and acc must not overlap");
+    if (s.rows == 0) return RA_OK;
+    return enqueue_partial(prob, s, kv_block_j, q, k, v, m, l, acc,
+                           static_cast<hipStream_t>(hip_stream));
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+static ra_status check_alias_exact(const void* out, const void* in1, const void* in2, size_t n,
+                                   const char* name) {
+  if ((out == in1) || (out == in2)) return RA_OK;
+  if (overlap(out, n, in1, n) || overlap(out, n, in2, n))
+    return fail(RA_ERR_INVALID_ARG, "%s partially overlaps an input", name);
+  return RA_OK;
+}
+
+ra_status ra_merge_partials(int64_t rows, int32_t head_dim, const float* m1, const float* l1,
+                            const float* acc1, const float* m2, const float* l2,
+                            const float* acc2, float* m_out, float* l_out, float* acc_out,
+                            void* hip_stream) {
+  try {
+    if (rows < 0) return fail(RA_ERR_INVALID_ARG, "rows %lld < 0", (long long)rows);
+    if (head_dim <= 0) return fail(RA_ERR_INVALID_ARG, "head_dim %d <= 0", head_dim);
+    if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+      return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (16, 32, 64, 128)", head_dim);
+    if (rows > (int64_t(1) << 40)) return fail(RA_ERR_INVALID_ARG, "rows too large");
+    const size_t rb = rows * 4, ab = rows * head_dim * 4;
+    ra_status st;
+    if ((st = check_ptr(m1, rb, "m1")) || (st = check_ptr(l1, rb, "l1")) ||
+        (st = check_ptr(acc1, ab, "acc1")) || (st = check_ptr(m2, rb, "m2")) ||
+        (st = check_ptr(l2, rb, "l2")) || (st = check_ptr(acc2, ab, "acc2")) ||
+        (st = check_ptr(m_out, rb, "m_out")) || (st = check_ptr(l_out, rb, "l_out")) ||
+        (st = check_ptr(acc_out, ab, "acc_out")))
+      return st;
+    if ((st = check_alias_exact(m_out, m1, m2, rb, "m_out")) ||
+        (st = check_alias_exact(l_out, l1, l2, rb, "l_out")) ||
+        (st = check_alias_exact(acc_out, acc1, acc2, ab, "acc_out")))
+      return st;
+    if (overlap(m_out, rb, l_out, rb) || overlap(m_out, rb, acc_out, ab) ||
+        overlap(l_out, rb, acc_out, ab))
+      return fail(RA_ERR_INVALID_ARG, "m_out, l_out and acc_out must not overlap");
+    if (rows == 0) return RA_OK;
+    hipError_t e = ra::launch_merge(rows, head_dim, m1, l1, acc1, m2, l2, acc2, m_out, l_out,
+                                    acc_out, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+ra_status ra_finalize(int64_t rows, int32_t head_dim, const float* m, const float* l, float* acc,
+                      float* lse, void* hip_stream) {
+  try {
+    if (rows < 0) return fail(RA_ERR_INVALID_ARG, "rows %lld < 0", (long long)rows);
+    if (head_dim <= 0) return fail(RA_ERR_INVALID_ARG, "head_dim %d <= 0", head_dim);
+    if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+      return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (16, 32, 64, 128)", head_dim);
+    if (rows > (int64_t(1) << 40)) return fail(RA_ERR_INVALID_ARG, "rows too large");
+    const size_t rb = rows * 4, ab = rows * head_dim * 4;
+    ra_status st;
+    if ((st = check_ptr(m, rb, "m")) || (st = check_ptr(l, rb, "l")) ||
+        (st = check_ptr(acc, ab, "acc")))
+      return st;
+    if (lse != nullptr && (st = check_ptr(lse, rb, "lse"))) return st;
+    if (lse != nullptr && (overlap(lse, rb, acc, ab) || overlap(lse, rb, m, rb) ||
+                           overlap(lse, rb, l, rb)))
+      return fail(RA_ERR_INVALID_ARG, "lse must not overlap m, l or acc");
+    if (rows == 0) return RA_OK;
+    hipError_t e =
+        ra::launch_finalize(rows, head_dim, m, l, acc, lse, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+size_t ra_ring_workspace_bytes(const ra_problem* prob) {
+  try {
+    Shape s;
+    if (validate_problem(prob, &s) != RA_OK) return 0;
+    return ws_layout(prob, s).total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, const void* v,
+                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    const int n = prob->n_ring;
+    const size_t qb = s.q_elems * s.elem;
+    const size_t blk = s.kv_elems * s.elem;
+    const size_t kvb = blk * n;
+    const size_t ob = s.q_elems * 4, rb = s.rows * 4;
+    if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kvb, "k")) ||
+        (st = check_ptr(v, kvb, "v")) || (st = check_ptr(out, ob, "out")))
+      return st;
+    if (lse != nullptr && (st = check_ptr(lse, rb, "lse"))) return st;
+    if (blk % 16 != 0 && n > 1)
+      return fail(RA_ERR_INVALID_ARG, "one KV block (%zu bytes) must be a multiple of 16 bytes",
+                  blk);
+    const WsLayout w = ws_layout(prob, s);
+    if (s.rows > 0) {
+      if (workspace == nullptr || workspace_bytes < w.total)
+        return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+      if (!aligned16(workspace))
+        return fail(RA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    }
+    const void* ins[3] = {q, k, v};
+    const size_t insz[3] = {qb, kvb, kvb};
+    for (int i = 0; i < 3; ++i) {
+      if (overlap(out, ob, ins[i], insz[i]))
+        return fail(RA_ERR_INVALID_ARG, "out must not overlap q, k or v");
+      if (lse && overlap(lse, rb, ins[i], insz[i]))
+        return fail(RA_ERR_INVALID_ARG, "lse must not overlap q, k or v");
+      if (s.rows > 0 && overlap(workspace, w.total, ins[i], insz[i]))
+        return fail(RA_ERR_INVALID_ARG, "workspace must not overlap q, k or v");
+    }
+    if (lse && overlap(lse, rb, out, ob)) return fail(RA_ERR_INVALID_ARG, "lse overlaps out");
+    if (s.rows > 0 && (overlap(workspace, w.total, out, ob) ||
+                       (lse && overlap(workspace, w.total, lse, rb))))
+      return fail(RA_ERR_INVALID_ARG, "workspace must not overlap out or lse");
+    if (s.rows == 0) return RA_OK;
+
+    // ---- enqueue -------------------------------------------------------
+    hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+    hipStream_t xs = static_cast<hipStream_t>(copy_stream);
+    const bool sep = xs != nullptr && xs != cs;
+    DeviceEvents* de = nullptr;
+    if ((st = get_events(&de)) != RA_OK) return st;
+    std::lock_guard<std::mutex> lk(de->mu);
+    if ((st = init_events(de)) != RA_OK) return st;
+
+    char* ws = static_cast<char*>(workspace);
+    const char* kbase = static_cast<const char*>(k);
+    const char* vbase = static_cast<const char*>(v);
+    char* stage_k[2] = {ws + w.stage_k[0], ws + w.stage_k[1]};
+    char* stage_v[2] = {ws + w.stage_v[0], ws + w.stage_v[1]};
+    float* pm = reinterpret_cast<float*>(ws + w.pm);
+    float* pl = reinterpret_cast<float*>(ws + w.pl);
+    float* pacc = reinterpret_cast<float*>(ws + w.pacc);
+    float* rm = reinterpret_cast<float*>(ws + w.rm);
+    float* rl = reinterpret_cast<float*>(ws + w.rl);
+    auto block_of = [&](int step) { return ((prob->rank - step) % n + n) % n; };
+    hipError_t e;
+    hipStream_t copy_on = sep ? xs : cs;
+
+    if (sep) {
+      if ((e = hipEventRecord(de->entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipStreamWaitEvent(xs, de->entry, 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+    }
+    auto stage = [&](int step) -> ra_status {
+      const int j = block_of(step), b = step % 2;
+      hipError_t e2 = hipMemcpyAsync(stage_k[b], kbase + (size_t)j * blk, blk,
+                                     hipMemcpyDeviceToDevice, copy_on);
+      if (e2 == hipSuccess)
+        e2 = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice,
+                            copy_on);
+      if (e2 != hipSuccess) return hip_fail(e2, "staging hipMemcpyAsync");
+      if (sep && (e2 = hipEventRecord(de->copy_done[b], xs)) != hipSuccess)
+        return hip_fail(e2, "hipEventRecord");
+      return RA_OK;
+    };
+
+    // step 0: the local block, read in place, written straight into the
+    // running state (m, l, out)
+    const int j0 = block_of(0);
+    if ((st = enqueue_partial(prob, s, j0, q, kbase + (size_t)j0 * blk, vbase + (size_t)j0 * blk,
+                              rm, rl, out, cs)) != RA_OK)
+      return st;
+    if (n > 1 && (st = stage(1)) != RA_OK) return st;
+
+    for (int step = 1; step < n; ++step) {
+      if (step + 1 < n) {
+        // buffer (step+1)%2 was last read by step-1 (steps >= 1 read staging)
+        if (sep && step - 1 >= 1 &&
+            (e = hipStreamWaitEvent(xs, de->compute_done[(step - 1) % 2], 0)) != hipSuccess)
+          return hip_fail(e, "hipStreamWaitEvent");
+        if ((st = stage(step + 1)) != RA_OK) return st;
+      }
+      const int b = step % 2;
+      if (sep && (e = hipStreamWaitEvent(cs, de->copy_done[b], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      const int j = block_of(step);
+      ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, j);
+      if (g.kind != ra::kNoneVisible && prob->kv_len > 0) {
+        if ((st = enqueue_partial(prob, s, j, q, stage_k[b], stage_v[b], pm, pl, pacc, cs)) !=
+            RA_OK)
+          return st;
+        e = ra::launch_merge(s.rows, prob->head_dim, rm, rl, out, pm, pl, pacc, rm, rl, out, cs);
+        if (e != hipSuccess) return hip_fail(e, "merge launch");
+      }
+      if (sep && (e = hipEventRecord(de->compute_done[b], cs)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord");
+    }
+    e = ra::launch_finalize(s.rows, prob->head_dim, rm, rl, out, lse, cs);
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int32_t ra_tile_class_host(const ra_problem* prob, int32_t kv_block_j, int64_t a_lo, int64_t a_hi,
+                           int64_t b_lo, int64_t b_hi) {
+  Shape s;
+  if (validate_problem(prob, &s) != RA_OK) return -1;
+  if (kv_block_j < 0 || kv_block_j >= prob->n_ring) {
+    fail(RA_ERR_INVALID_ARG, "kv_block_j out of range");
+    return -1;
+  }
+  if (a_lo < 0 || a_hi < a_lo || a_hi >= prob->q_len || b_lo < 0 || b_hi < b_lo ||
+      b_hi >= prob->kv_len) {
+    fail(RA_ERR_INVALID_ARG, "tile bounds out of range");
+    return -1;
+  }
+  ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, kv_block_j);
+  return ra::tile_class(g, a_lo, a_hi, b_lo, b_hi);
+}
+
+static ra_status check_tiles(const ra_problem* prob, int32_t j, int32_t tq, int32_t tk,
+                             Shape* s) {
+  ra_status st = validate_problem(prob, s);
+  if (st != RA_OK) return st;
+  if (j < 0 || j >= prob->n_ring) return fail(RA_ERR_INVALID_ARG, "kv_block_j out of range");
+  if (tq < 1 || tk < 1) return fail(RA_ERR_INVALID_ARG, "tile sizes must be >= 1");
+  const int64_t nqt = (prob->q_len + tq - 1) / tq, nkt = (prob->kv_len + tk - 1) / tk;
+  if (nqt * nkt > (int64_t(1) << 34)) return fail(RA_ERR_INVALID_ARG, "too many tiles");
+  return RA_OK;
+}
+
+ra_status ra_tile_classes_host(const ra_problem* prob, int32_t kv_block_j, int32_t tq, int32_t tk,
+                               int8_t* out_host) {
+  try {
+    Shape s;
+    ra_status st = check_tiles(prob, kv_block_j, tq, tk, &s);
+    if (st != RA_OK) return st;
+    const int64_t nqt = (prob->q_len + tq - 1) / tq, nkt = (prob->kv_len + tk - 1) / tk;
+    if (nqt * nkt > 0 && out_host == nullptr) return fail(RA_ERR_INVALID_ARG, "out is NULL");
+    ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, kv_block_j);
+    for (int64_t qt = 0; qt < nqt; ++qt) {
+      const int64_t a_lo = qt * tq, a_hi = std::min<int64_t>(a_lo + tq, prob->q_len) - 1;
+      for (int64_t kt = 0; kt < nkt; ++kt) {
+        const int64_t b_lo = kt * tk, b_hi = std::min<int64_t>(b_lo + tk, prob->kv_len) - 1;
+        out_host[qt * nkt + kt] = (int8_t)ra::tile_class(g, a_lo, a_hi, b_lo, b_hi);
+      }
+    }
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+ra_status ra_tile_classes_device(const ra_problem* prob, int32_t kv_block_j, int32_t tq,
+                                 int32_t tk, int8_t* out_device, void* hip_stream) {
+  try {
+    Shape s;
+    ra_status st = check_tiles(prob, kv_block_j, tq, tk, &s);
+    if (st != RA_OK) return st;
+    const int64_t nqt = (prob->q_len + tq - 1) / tq, nkt = (prob->kv_len + tk - 1) / tk;
+    if (nqt * nkt == 0) return RA_OK;
+    if (out_device == nullptr) return fail(RA_ERR_INVALID_ARG, "out is NULL");
+    ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, kv_block_j);
+    hipError_t e = ra::launch_tile_classes(g.kind, g.delta, prob->q_len, prob->kv_len, tq, tk,
+                                           out_device, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "tile_classes launch");
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+}  // extern "C"

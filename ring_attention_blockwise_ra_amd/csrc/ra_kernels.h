@@ -1,0 +1,47 @@
+// ra_kernels.h -- launch interface between the C ABI layer and the kernels
+// (library-internal; not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+struct AttnParams {
+  const void* q;        // [batch, q_len, hq, D]
+  const void* k;        // [batch, kv_len, hkv, D] (one block)
+  const void* v;
+  float* m;             // [batch, q_len, hq]
+  float* l;
+  float* acc;           // [batch, q_len, hq, D]
+  int64_t q_bstride;    // elements per batch of q
+  int64_t kv_bstride;   // elements per batch of k / v
+  int32_t batch;
+  int32_t q_len;
+  int32_t kv_len;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t group;        // hq / hkv
+  int32_t rows_per_bg;  // group * q_len: query rows sharing one KV head
+  int32_t n_row_tiles;  // set by the launcher
+  int32_t geom_kind;    // ra::BlockKind
+  int32_t geom_delta;
+  float scale_log2;     // scale * log2(e)
+};
+
+// qb: query blocks of 32 rows per wavefront in the bf16 kernel (1 or 2).
+hipError_t launch_attention(const AttnParams& p, int is_bf16, int qb, hipStream_t stream);
+int bf16_rows_per_wg(int qb);
+
+hipError_t launch_merge(int64_t rows, int d, const float* m1, const float* l1, const float* a1,
+                        const float* m2, const float* l2, const float* a2, float* mo, float* lo,
+                        float* ao, hipStream_t stream);
+hipError_t launch_finalize(int64_t rows, int d, const float* m, const float* l, float* acc,
+                           float* lse, hipStream_t stream);
+hipError_t launch_fill_empty(int64_t rows, int d, float* m, float* l, float* acc,
+                             hipStream_t stream);
+hipError_t launch_tile_classes(int kind, int delta, int64_t q_len, int64_t kv_len, int tq, int tk,
+                               int8_t* out, hipStream_t stream);
+
+}  // namespace ra

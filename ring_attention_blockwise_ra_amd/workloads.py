@@ -1,0 +1,69 @@
+"""The named workloads as device tensors, ready for the library.
+
+Builds one device's share (q) and the N K/V blocks of a workload in the
+layout's token order from the seeded global-order generators, and computes the
+work a share represents (visible query/key pairs, counted FLOPs) for
+throughput reporting. Holds no attention arithmetic.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import synth
+from .layout import blocks_from_global, share_tokens
+
+
+def visible_pairs(layout: str, causal: bool, n_ring: int, rank: int, block_len: int) -> int:
+    """Unmasked (query, key) pairs of one share over all N blocks, per head and
+    batch row: non-causal N*B^2; contiguous causal r*B^2 + B(B+1)/2 (blocks
+    before the share fully visible, its own block a triangle); striped causal
+    N*B(B-1)/2 + (r+1)*B (every block a triangle, blocks after the share
+    without their diagonal)."""
+    n, b, r = n_ring, block_len, rank
+    if not causal:
+        return n * b * b
+    if layout == "contiguous":
+        return r * b * b + b * (b + 1) // 2
+    return n * b * (b - 1) // 2 + (r + 1) * b
+
+
+def counted_flops(layout, causal, n_ring, rank, block_len, hq, head_dim, batch=1) -> int:
+    """4*d FLOPs (2d for q.k, 2d for p*v) per visible pair per query head."""
+    return 4 * head_dim * hq * batch * visible_pairs(layout, causal, n_ring, rank, block_len)
+
+
+def prepare(cfg_name: str, layout: str, rank: int, device="cuda", keep_global: bool = False):
+    """Device tensors of one share of a named workload.
+
+    Returns a dict with q [1, B, hq, d], k/v [N, 1, B, hkv, d] (layout order),
+    q_tokens (global token index of each local query row), the config dict,
+    and, when keep_global, the global-order k and v.
+    """
+    c = synth.CONFIGS[cfg_name]
+    n, blen = c["n_ring"], c["block"]
+    q_tok = share_tokens(layout, n, rank, blen, device="cpu")
+    q, k_glob, v_glob = synth.config_global(cfg_name, device=device, q_rows=q_tok.to(device))
+    kb = blocks_from_global(k_glob, layout, n)
+    vb = blocks_from_global(v_glob, layout, n)
+    out = dict(cfg=c, q=q.contiguous(), k=kb, v=vb, q_tokens=q_tok, layout=layout, rank=rank)
+    if keep_global:
+        out["k_global"], out["v_global"] = k_glob, v_glob
+    else:
+        del k_glob, v_glob
+    return out
+
+
+def sample_rows(block_len: int, n: int, seed: int = 0, tile_edges=(128, 256)) -> torch.Tensor:
+    """Local query rows to check at full size: the first 8, the last 8, rows on
+    both sides of tile edges, and seeded random rows, up to n in total."""
+    rows = set(range(min(8, block_len)))
+    rows |= set(range(max(0, block_len - 8), block_len))
+    for t in tile_edges:
+        for e in (t - 1, t, 2 * t - 1, 2 * t, block_len // 2 - 1, block_len // 2):
+            if 0 <= e < block_len:
+                rows.add(e)
+    g = torch.Generator().manual_seed(seed)
+    while len(rows) < min(n, block_len):
+        rows.add(int(torch.randint(0, block_len, (1,), generator=g)))
+    return torch.tensor(sorted(rows)[:max(n, 0)], dtype=torch.int64)

@@ -1,0 +1,194 @@
+"""CPU-only tests of the HIP library's host side: it loads, exports every
+symbol include/ra.h declares, validates arguments before any HIP call, and its
+causal tile scheduler (host mirror) matches the oracle's element brute force
+bit for bit. No compute call is made (there may be no GPU)."""
+
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import ring_oracle as orc
+from ring_attention_blockwise_ra_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+_ORACLE_CLASS = {B.RA_TILE_SKIP: orc.SKIP, B.RA_TILE_PARTIAL: orc.PARTIAL, B.RA_TILE_FULL: orc.FULL}
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from ring_attention_blockwise_ra_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 9
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _prob(**kw):
+    base = dict(dtype=B.RA_BF16, batch=1, hq=4, hkv=2, head_dim=64, q_len=256, kv_len=256,
+                n_ring=4, rank=1, causal=1, layout="contiguous")
+    base.update(kw)
+    return B.make_problem(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def _partial(L, prob, j=0, ptr=FAKE):
+    return L.ra_block_attn_partial(ctypes.byref(prob), j, ptr, ptr, ptr, ptr, ptr, ptr, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), B.RA_ERR_INVALID_ARG),
+    (dict(batch=-1), B.RA_ERR_INVALID_ARG),
+    (dict(hq=0), B.RA_ERR_INVALID_ARG),
+    (dict(hq=6, hkv=4), B.RA_ERR_INVALID_ARG),
+    (dict(head_dim=96), B.RA_ERR_UNSUPPORTED),
+    (dict(head_dim=256), B.RA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), B.RA_ERR_INVALID_ARG),
+    (dict(n_ring=0, rank=0), B.RA_ERR_INVALID_ARG),
+    (dict(rank=4), B.RA_ERR_INVALID_ARG),
+    (dict(rank=-1), B.RA_ERR_INVALID_ARG),
+    (dict(q_len=128), B.RA_ERR_INVALID_ARG),          # causal needs q_len == kv_len
+    (dict(q_len=-5, causal=0), B.RA_ERR_INVALID_ARG),
+    (dict(q_len=(1 << 30) + 1, kv_len=(1 << 30) + 1), B.RA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.RA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), B.RA_ERR_INVALID_ARG),
+])
+def test_problem_validation_before_any_hip_call(L, kw, status):
+    prob = _prob(**kw)
+    assert _partial(L, prob) == status
+    assert L.ra_last_error()  # message set
+    assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) == 0
+
+
+def test_bad_layout_and_causal_flags(L):
+    prob = _prob()
+    prob.layout = 5
+    assert _partial(L, prob) == B.RA_ERR_INVALID_ARG
+    prob = _prob()
+    prob.causal = 2
+    assert _partial(L, prob) == B.RA_ERR_INVALID_ARG
+
+
+def test_pointer_checks(L):
+    prob = _prob()
+    assert L.ra_block_attn_partial(ctypes.byref(prob), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.RA_ERR_INVALID_ARG
+    assert b"q is NULL" in L.ra_last_error()
+    odd = ctypes.c_void_p(0x10008)
+    assert L.ra_block_attn_partial(ctypes.byref(prob), 0, FAKE, odd, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.RA_ERR_INVALID_ARG
+    assert b"aligned" in L.ra_last_error()
+    # j out of range
+    assert _partial(L, prob, j=4) == B.RA_ERR_INVALID_ARG
+    assert L.ra_block_attn_partial(ctypes.byref(prob), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.RA_ERR_INVALID_ARG
+    assert L.ra_block_attn_partial(None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) \
+        == B.RA_ERR_INVALID_ARG
+
+
+def test_output_aliasing_rejected(L):
+    prob = _prob()
+    base = 0x100000
+    q = ctypes.c_void_p(base)
+    acc = ctypes.c_void_p(base + 64)  # inside q
+    other = ctypes.c_void_p(0x40000000)
+    st = L.ra_block_attn_partial(ctypes.byref(prob), 0, q, other, other, ctypes.c_void_p(0x50000000),
+                                 ctypes.c_void_p(0x60000000), acc, None)
+    assert st == B.RA_ERR_INVALID_ARG
+    assert b"overlap" in L.ra_last_error()
+
+
+def test_merge_validation(L):
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(9)]
+    assert L.ra_merge_partials(-1, 64, *p, None) == B.RA_ERR_INVALID_ARG
+    assert L.ra_merge_partials(10, 48, *p, None) == B.RA_ERR_UNSUPPORTED
+    # acc_out partially overlapping acc1 is rejected, exact aliasing is allowed (and then
+    # the call would run, so only the rejection is checked here)
+    q = list(p)
+    q[8] = ctypes.c_void_p(p[2].value + 16)
+    assert L.ra_merge_partials(10, 64, *q, None) == B.RA_ERR_INVALID_ARG
+    # rows == 0: nothing to do, no HIP call
+    assert L.ra_merge_partials(0, 64, *p, None) == B.RA_OK
+    assert L.ra_finalize(-2, 64, p[0], p[1], p[2], None, None) == B.RA_ERR_INVALID_ARG
+    assert L.ra_finalize(0, 64, p[0], p[1], p[2], None, None) == B.RA_OK
+
+
+def test_ring_workspace_size_and_checks(L):
+    prob = _prob(batch=2, hq=8, hkv=2, head_dim=128, q_len=1000, kv_len=1000, n_ring=8, rank=7)
+    got = L.ra_ring_workspace_bytes(ctypes.byref(prob))
+    blk = 2 * 1000 * 2 * 128 * 2
+    rows = 2 * 1000 * 8
+    def a(x):
+        return (x + 255) // 256 * 256
+    want = 4 * a(blk) + 4 * a(rows * 4) + a(rows * 128 * 4)
+    assert got == want
+    ws_small = ctypes.c_size_t(got - 1)
+    buf = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(5)]
+    st = L.ra_ring_fwd(ctypes.byref(prob), buf[0], buf[1], buf[2], buf[3], None, buf[4],
+                       ws_small, None, None)
+    assert st == B.RA_ERR_WORKSPACE
+    st = L.ra_ring_fwd(ctypes.byref(prob), buf[0], buf[1], buf[2], buf[3], None, None,
+                       ctypes.c_size_t(got), None, None)
+    assert st == B.RA_ERR_WORKSPACE
+    # empty share: nothing to do
+    empty = _prob(q_len=0, kv_len=0)
+    assert L.ra_ring_fwd(ctypes.byref(empty), None, None, None, None, None, None, 0, None, None) \
+        == B.RA_OK
+
+
+# ---- causal tile scheduler: host mirror vs oracle brute force --------------
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_tile_classes_host_match_bruteforce(L, layout):
+    sizes = [1, 2, 4, 8, 16]
+    for n, blen in [(2, 8), (3, 13), (4, 16), (8, 9), (1, 5)]:
+        for tq, tk in itertools.product(sizes, sizes):
+            for r, j in itertools.product(range(n), range(n)):
+                for causal in (True, False):
+                    prob = _prob(n_ring=n, rank=r, q_len=blen, kv_len=blen, causal=causal,
+                                 layout=layout)
+                    got = B.ra_tile_classes_host(prob, j, tq, tk)
+                    want = orc.tile_classes_bruteforce(layout, causal, n, r, j, blen, blen, tq, tk)
+                    mapped = np.vectorize(_ORACLE_CLASS.get)(got)
+                    np.testing.assert_array_equal(mapped, want)
+
+
+def test_tile_classes_host_real_size_counts(L):
+    """1M-token share, 8 blocks of 131072, 128x128 tiles: host mirror counts vs
+    the oracle's closed-form counts for every (layout, rank, block)."""
+    blen, t = 131072, 128
+    for layout in ("contiguous", "striped"):
+        for r, j in itertools.product([0, 3, 7], range(8)):
+            prob = _prob(n_ring=8, rank=r, q_len=blen, kv_len=blen, layout=layout)
+            got = B.ra_tile_classes_host(prob, j, t, t)
+            counts = (int((got == B.RA_TILE_FULL).sum()), int((got == B.RA_TILE_PARTIAL).sum()),
+                      int((got == B.RA_TILE_SKIP).sum()))
+            assert counts == orc.tile_class_counts(layout, True, 8, r, j, blen, blen, t, t)
+
+
+def test_tile_class_single(L):
+    prob = _prob(n_ring=8, rank=3, q_len=16, kv_len=16, layout="striped")
+    assert B.ra_tile_class_host(prob, 5, 4, 7, 4, 7) == B.RA_TILE_PARTIAL  # delta 1 diagonal
+    assert B.ra_tile_class_host(prob, 5, 4, 7, 0, 3) == B.RA_TILE_FULL
+    assert B.ra_tile_class_host(prob, 5, 0, 3, 4, 7) == B.RA_TILE_SKIP
+    with pytest.raises(B.RaError):
+        B.ra_tile_class_host(prob, 5, 0, 16, 0, 3)
