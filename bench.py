@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark of one device's share of Ring Attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+A step is one full pass of the hot path over the workload: ra_ring_fwd for
+the share (8 ring steps: partial attention per block, staging copies on a
+side stream, merges, finalize). For the 1M-token causal workload (c4, the
+default) a step runs the rank-7 share in both token layouts, contiguous then
+striped. Inputs are resident in HBM before timing starts.
+
+Printed (one JSON line): TFLOP/s over causal-counted FLOPs (4*d per visible
+(query, key) pair per query head), the roofline of the attention kernel
+(its FLOPs per launch over its average launch time, measured with HIP events
+on its own stream), copy/compute overlap of the staged ring, merge-kernel
+HBM bandwidth, and the fp64 CPU oracle timed on a bounded sample of the same
+workload (a reported baseline, not a target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from ring_attention_blockwise_ra_amd import binding as B  # noqa: E402
+from ring_attention_blockwise_ra_amd import synth, workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+KERNEL_SOURCES = ["ring_attention_blockwise_ra_amd/csrc/ra_kernels.hip",
+                  "ring_attention_blockwise_ra_amd/csrc/ra_sched.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_bf16_mfma_c4_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def timed(fn, stream=None):
+    """Run fn once between two HIP events on `stream`; returns ms."""
+    s = stream or torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def ring_call(w, out, lse, ws, copy_stream="auto"):
+    c = w["cfg"]
+    return B.ra_ring_fwd(w["q"], w["k"], w["v"], n_ring=c["n_ring"], causal=c["causal"],
+                         layout=w["layout"], rank=w["rank"], out=out, lse=lse, workspace=ws,
+                         copy_stream=copy_stream)
+
+
+def kernel_leg(w):
+    """Attention kernel alone: one launch per computed block, HIP events on
+    the launch stream. Returns (total counted FLOPs, total ms, launches)."""
+    c = w["cfg"]
+    n, r, blen = c["n_ring"], w["rank"], c["block"]
+    q = w["q"]
+    b, lq, hq, d = q.shape
+    m = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device)
+    l = torch.empty_like(m)
+    acc = torch.empty(b, lq, hq, d, dtype=torch.float32, device=q.device)
+    flops = ms = 0.0
+    launches = 0
+    for s in range(n):
+        j = (r - s) % n
+        pairs = block_pairs(w["layout"], c["causal"], n, r, j, blen)
+        if pairs == 0:
+            continue
+        ms += timed(lambda: B.ra_block_attn_partial(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
+                                                     causal=c["causal"], layout=w["layout"],
+                                                     m=m, l=l, acc=acc))
+        flops += 4.0 * d * hq * b * pairs
+        launches += 1
+    return flops, ms, launches
+
+
+def block_pairs(layout, causal, n, r, j, blen):
+    """Visible pairs of one (share, block) per head: full, none, or a
+    triangle with or without its diagonal."""
+    if not causal:
+        return blen * blen
+    if layout == "contiguous":
+        if j < r:
+            return blen * blen
+        if j > r:
+            return 0
+        return blen * (blen + 1) // 2
+    return blen * (blen + 1) // 2 if j <= r else blen * (blen - 1) // 2
+
+
+def overlap_leg(w, out, lse, ws, reps=2):
+    """T_ring (copies on a side stream), T_nocopy (same kernels reading the
+    source blocks in place, through the public entry points), T_copy (the
+    N-1 staging copies alone). efficiency = 1 - max(0, T_ring - T_nocopy)/T_copy."""
+    c = w["cfg"]
+    n, r = c["n_ring"], w["rank"]
+    q = w["q"]
+    b, lq, hq, d = q.shape
+    pm = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device)
+    pl, rm, rl = torch.empty_like(pm), torch.empty_like(pm), torch.empty_like(pm)
+    pacc = torch.empty(b, lq, hq, d, dtype=torch.float32, device=q.device)
+
+    def nocopy():
+        B.ra_block_attn_partial(q, w["k"][r], w["v"][r], r, n_ring=n, rank=r, causal=c["causal"],
+                                layout=w["layout"], m=rm, l=rl, acc=out)
+        for s in range(1, n):
+            j = (r - s) % n
+            if block_pairs(w["layout"], c["causal"], n, r, j, c["block"]) == 0:
+                continue
+            B.ra_block_attn_partial(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
+                                    causal=c["causal"], layout=w["layout"], m=pm, l=pl, acc=pacc)
+            B.ra_merge_partials(rm, rl, out, pm, pl, pacc, out=(rm, rl, out))
+        B.ra_finalize(rm, rl, out, lse=lse)
+
+    stage_k = torch.empty_like(w["k"][0])
+    stage_v = torch.empty_like(w["v"][0])
+
+    def copies():
+        for s in range(1, n):
+            j = (r - s) % n
+            stage_k.copy_(w["k"][j])
+            stage_v.copy_(w["v"][j])
+
+    t_ring = min(timed(lambda: ring_call(w, out, lse, ws)) for _ in range(reps))
+    t_nocopy = min(timed(nocopy) for _ in range(reps))
+    t_copy = min(timed(copies) for _ in range(reps))
+    eff = 1.0 - max(0.0, t_ring - t_nocopy) / t_copy if t_copy > 0 else 1.0
+    return dict(efficiency=round(eff, 4), t_ring_ms=round(t_ring, 3),
+                t_nocopy_ms=round(t_nocopy, 3), t_copy_ms=round(t_copy, 3),
+                copy_bytes=int(2 * (n - 1) * w["k"][0].numel() * w["k"].element_size()))
+
+
+def merge_leg(w, reps=5):
+    q = w["q"]
+    b, lq, hq, d = q.shape
+    rows = b * lq * hq
+    g = torch.Generator(device=q.device).manual_seed(1)
+    parts = []
+    for _ in range(2):
+        m = torch.randn(b, lq, hq, device=q.device, generator=g)
+        l = torch.rand(b, lq, hq, device=q.device, generator=g) + 1
+        a = torch.randn(b, lq, hq, d, device=q.device, generator=g)
+        parts.append((m, l, a))
+    out = (torch.empty_like(parts[0][0]), torch.empty_like(parts[0][1]),
+           torch.empty_like(parts[0][2]))
+    B.ra_merge_partials(*parts[0], *parts[1], out=out)
+    ms = min(timed(lambda: B.ra_merge_partials(*parts[0], *parts[1], out=out)) for _ in range(reps))
+    nbytes = 3 * rows * (4 * d + 8)
+    return dict(gbs=round(nbytes / ms / 1e6, 1), ms=round(ms, 4), bytes=nbytes,
+                frac_of_peak=round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4))
+
+
+def cpu_baseline_leg(w, n_rows, k_global, v_global):
+    """The fp64 oracle (untuned) on n_rows sampled query rows x all heads of
+    the share; rate in counted TFLOP/s of those rows."""
+    import numpy as np
+    from oracle import ring_oracle as orc
+    c = w["cfg"]
+    rows = workloads.sample_rows(c["block"], n_rows, seed=3)
+    tok = w["q_tokens"][rows]
+    q_rows = w["q"][:, rows.to(w["q"].device)].to(torch.float64).cpu().numpy()
+    kmax = int(tok.max()) + 1 if c["causal"] else k_global.shape[1]
+    k64 = k_global[:, :kmax].to(torch.float64).cpu().numpy()
+    v64 = v_global[:, :kmax].to(torch.float64).cpu().numpy()
+    t0 = time.perf_counter()
+    orc.naive_attention_rows(q_rows, tok.numpy(), k64, v64, c["causal"])
+    dt = time.perf_counter() - t0
+    pairs = int((tok + 1).sum()) if c["causal"] else len(tok) * k_global.shape[1]
+    flops = 4.0 * c["d"] * c["hq"] * pairs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads),
+                kind="oracle",
+                sample=(f"{len(tok)} query rows x {c['hq']} heads of the {w['layout']} rank-{w['rank']}"
+                        f" share, all visible keys, fp64 NumPy; {dt:.1f} s"),
+                seconds=round(dt, 2), host_cpus=len(os.sched_getaffinity(0)))
+
+
+def load_counters(src_hash):
+    """HBM traffic per attention launch from committed rocprofv3 counter runs,
+    only if they were taken on the current kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != src_hash:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="c4", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--layouts", default=None, help="comma list; default: the workload's")
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the timed steps (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the ring; runs on more than one GPU are "
+              "not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    c = synth.CONFIGS[args.workload]
+    layouts = args.layouts.split(",") if args.layouts else list(c["layouts"])
+    rank = args.rank if args.rank is not None else c["ranks"][-1]
+    log(f"[bench] workload {args.workload} layouts {layouts} rank {rank}")
+
+    ws_list = []
+    for layout in layouts:
+        t0 = time.time()
+        w = workloads.prepare(args.workload, layout, rank, device=dev,
+                              keep_global=(not args.skip_cpu and layout == layouts[0]))
+        b, lq, hq, d = w["q"].shape
+        prob = B.make_problem(dtype=w["q"].dtype, batch=b, hq=hq, hkv=w["k"].shape[3],
+                              head_dim=d, q_len=lq, kv_len=w["k"].shape[2], n_ring=c["n_ring"],
+                              rank=rank, causal=c["causal"], layout=layout)
+        w["out"] = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev)
+        w["lse"] = torch.empty(b, lq, hq, dtype=torch.float32, device=dev)
+        w["ws"] = torch.empty(B.ra_ring_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+        w["flops"] = workloads.counted_flops(layout, c["causal"], c["n_ring"], rank, c["block"],
+                                             hq, d, b)
+        ws_list.append(w)
+        torch.cuda.synchronize()
+        log(f"[bench] prepared {layout} in {time.time() - t0:.1f}s")
+
+    def step():
+        for w in ws_list:
+            ring_call(w, w["out"], w["lse"], w["ws"])
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    torch.cuda.synchronize()
+    per_layout_ms = {w["layout"]: 0.0 for w in ws_list}
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        for w in ws_list:
+            per_layout_ms[w["layout"]] += timed(lambda: ring_call(w, w["out"], w["lse"], w["ws"]))
+        log(f"[bench] step {i + 1}/{args.steps} done")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    total_ms = sum(per_layout_ms.values())
+    ms_per_step = total_ms / args.steps
+    total_flops = sum(w["flops"] for w in ws_list) * args.steps
+    value = total_flops / (total_ms / 1e3) / 1e12
+
+    result = {
+        "metric": "ring-attn fwd TFLOP/s (causal-counted) + % bf16 MFMA peak, 1 GPU, "
+                  "causal 1M-token share",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1), bf16-rounded)",
+        "config": {
+            "workload": (f"{args.workload}: one device's share, N={c['n_ring']} blocks of "
+                         f"{c['block']} tokens, {'causal' if c['causal'] else 'non-causal'}, "
+                         f"rank {rank}, layouts {'+'.join(layouts)}"),
+            "seq_len": c["n_ring"] * c["block"], "block": c["block"], "n_ring": c["n_ring"],
+            "rank": rank, "hq": c["hq"], "hkv": c["hkv"], "head_dim": c["d"], "batch": 1,
+            "layouts": layouts,
+        },
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed": round(wall, 2),
+        "layouts": {
+            w["layout"]: {"ms": round(per_layout_ms[w["layout"]] / args.steps, 3),
+                          "tflops": round(w["flops"] / (per_layout_ms[w["layout"]] / args.steps / 1e3) / 1e12, 2),
+                          "counted_flops": w["flops"]}
+            for w in ws_list},
+    }
+
+    if not args.skip_extras:
+        # dominant kernel: the attention partial, launched once per computed block
+        kf = km = 0.0
+        nl = 0
+        for w in ws_list:
+            f, ms, n = kernel_leg(w)
+            kf += f
+            km += ms
+            nl += n
+        achieved = kf / (km / 1e3) / 1e12
+        src_hash = kernel_source_hash()
+        traffic = load_counters(src_hash)
+        result["roofline"] = {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_bf16_mfma<128,1>" if c["dtype"] == "bf16" else "attn_f32_fma",
+            "launches": nl, "avg_launch_ms": round(km / max(nl, 1), 3),
+            "flops_per_launch_avg": kf / max(nl, 1),
+            "kernel_source_hash": src_hash,
+        }
+        log("[bench] kernel leg done")
+        result["overlap"] = overlap_leg(ws_list[0], ws_list[0]["out"], ws_list[0]["lse"],
+                                        ws_list[0]["ws"])
+        log("[bench] overlap leg done")
+        result["merge"] = merge_leg(ws_list[0])
+        log("[bench] merge leg done")
+
+    if not args.skip_cpu:
+        w = ws_list[0]
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows ...")
+        result["cpu_baseline"] = cpu_baseline_leg(w, args.cpu_rows, w["k_global"], w["v_global"])
+        log("[bench] cpu baseline done")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
