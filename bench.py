@@ -175,7 +175,6 @@ def merge_leg(w, reps=5):
 def cpu_baseline_leg(w, n_rows, k_global, v_global):
     """The fp64 oracle (untuned) on n_rows sampled query rows x all heads of
     the share; rate in counted TFLOP/s of those rows."""
-    import numpy as np
     from oracle import ring_oracle as orc
     c = w["cfg"]
     rows = workloads.sample_rows(c["block"], n_rows, seed=3)
@@ -222,7 +221,7 @@ def main():
     ap.add_argument("--workload", default="c4", choices=sorted(synth.CONFIGS))
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--layouts", default=None, help="comma list; default: the workload's")
-    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the timed steps (for profiler runs)")
@@ -338,8 +337,13 @@ def main():
             "kernel_source_hash": src_hash,
         }
         log("[bench] kernel leg done")
-        result["overlap"] = overlap_leg(ws_list[0], ws_list[0]["out"], ws_list[0]["lse"],
-                                        ws_list[0]["ws"])
+        # every layout, so that the attention launches of the whole run have the
+        # same mix as the kernel leg (its average is compared with rocprofv3's)
+        ov = {w["layout"]: overlap_leg(w, w["out"], w["lse"], w["ws"]) for w in ws_list}
+        tot = {k: sum(o[k] for o in ov.values()) for k in ("t_ring_ms", "t_nocopy_ms", "t_copy_ms")}
+        eff = 1.0 - max(0.0, tot["t_ring_ms"] - tot["t_nocopy_ms"]) / tot["t_copy_ms"]
+        result["overlap"] = dict(efficiency=round(eff, 4), **{k: round(v, 3) for k, v in tot.items()},
+                                 per_layout=ov)
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
         log("[bench] merge leg done")

@@ -110,13 +110,14 @@ ra_status check_ptr(const void* p, size_t bytes, const char* name) {
   return RA_OK;
 }
 
-int env_qb() {
-  static int qb = [] {
-    const char* e = getenv("RA_QB");
-    if (e && (e[0] == '1' || e[0] == '2') && e[1] == 0) return e[0] - '0';
-    return 1;
+// Waves per workgroup of the bf16 kernel: 8 (two per SIMD) unless RA_WAVES=4.
+int env_waves() {
+  static int w = [] {
+    const char* e = getenv("RA_WAVES");
+    if (e && e[0] == '4' && e[1] == 0) return 4;
+    return 8;
   }();
-  return qb;
+  return w;
 }
 
 ra::AttnParams make_params(const ra_problem* p, const Shape& s, int32_t j, const void* q,
@@ -158,7 +159,7 @@ ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const 
     return RA_OK;
   }
   ra::AttnParams a = make_params(p, s, j, q, k, v, m, l, acc);
-  e = ra::launch_attention(a, p->dtype == RA_BF16, env_qb(), st);
+  e = ra::launch_attention(a, p->dtype == RA_BF16, env_waves(), st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RA_OK;
 }

@@ -30,9 +30,8 @@ struct AttnParams {
   float scale_log2;     // scale * log2(e)
 };
 
-// qb: query blocks of 32 rows per wavefront in the bf16 kernel (1 or 2).
-hipError_t launch_attention(const AttnParams& p, int is_bf16, int qb, hipStream_t stream);
-int bf16_rows_per_wg(int qb);
+// waves: wavefronts per workgroup of the bf16 kernel (4 or 8; 32 rows each).
+hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream);
 
 hipError_t launch_merge(int64_t rows, int d, const float* m1, const float* l1, const float* a1,
                         const float* m2, const float* l2, const float* a2, float* mo, float* lo,

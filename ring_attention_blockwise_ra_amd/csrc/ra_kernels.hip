@@ -12,7 +12,7 @@
 //        normaliser update, output rescaled the same way.
 //
 // Kernels
-//   attn_bf16_mfma<D, QB>  one KV block against the local queries, bf16 in,
+//   attn_bf16_mfma<D, NW>  one KV block against the local queries, bf16 in,
 //                          fp32 accumulate, v_mfma_f32_32x32x16_bf16 for both
 //                          contractions, K/V tiles staged through LDS,
 //                          in-register online softmax (exp2 domain).
@@ -50,9 +50,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //
 // Work decomposition. For batch b and KV head g the G = hq/hkv query heads of
 // the group share K/V; their rows are enumerated as rho = a*G + hh (a: local
-// query index, hh: head within the group). A workgroup of 4 waves owns
-// 128*QB consecutive rows rho and streams block j's K/V of head g through
-// LDS in tiles of TK keys; wave w owns rows [w*32*QB, (w+1)*32*QB) of them.
+// query index, hh: head within the group). A workgroup of NW waves owns 32*NW
+// consecutive rows rho (wave w: rows [32w, 32w+32)) and streams block j's K/V
+// of head g through LDS in tiles of 64 keys, double-buffered: the global
+// loads of tile t+1 are in flight while tile t is computed. With NW = 8 two
+// waves share each SIMD, so one wave's softmax (VALU) runs under the other's
+// MFMAs.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64):
 //   A operand: lane L holds A[m = L%32][k = 8*(L/32) .. +8]
@@ -62,108 +65,99 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // lane owns one query column: row max and row sum reduce over its own
 // registers plus one exchange with lane L^32. The output is also transposed,
 // O^T += V^T P^T (m = head dim, n = query): the rescale factor is per lane and
-// the P^T operand comes straight from the S^T accumulator registers. Within a
-// 16-key chunk, lane half h holds keys {4h..4h+3, 8+4h..8+4h+3}; V is stored
-// transposed in LDS with 4-key groups 1 and 2 of each chunk swapped so that
-// those eight keys are contiguous and the A operand is one 16-byte LDS read.
+// the P^T operand comes straight from the S^T accumulator registers: within a
+// 16-key chunk lane half h holds keys {4h..4h+3, 8+4h..8+4h+3}, which fixes
+// the order of the reduction slots. K and V are stored row-major in LDS
+// (head_dim contiguous). The K operand is one 16-byte read per lane. The V^T
+// operand is gathered with two ds_read_b64_tr_b16 per MFMA: inside each group
+// of 16 lanes that instruction hands output lane i, element j, the (i%4)-th
+// 16-bit element of the 8 bytes addressed by source lane 4j + i/4. Source lane
+// s therefore addresses V[k0 + s/4][d0 + 4(s%4)], and output lane i receives
+// V[k0 .. k0+3][d0 + i]: four consecutive keys of one head dimension.
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // workgroup size of the fp32 and elementwise kernels
 constexpr int kTK = 64;
 
 template <int D>
 struct BfTile {
-  static constexpr int DP = D < 32 ? 32 : D;       // rows of V^T (MFMA M >= 32)
-  static constexpr int KS = D + 8;                 // K row stride (bf16), pad vs bank conflicts
-  static constexpr int VS = kTK + 8;               // V^T row stride (bf16)
+  static constexpr int DP = D < 32 ? 32 : D;       // head dims padded to the MFMA M of 32
+  static constexpr int KS = D + 8;                 // K row stride (bf16): 16-byte reads
+                                                   // of 8 rows hit distinct banks
+  static constexpr int VS = DP + 16;               // V row stride (bf16): the 4 rows of a
+                                                   // transposed read hit distinct banks
   static constexpr int K_ELEMS = kTK * KS;
-  static constexpr int V_ELEMS = DP * VS;
+  static constexpr int V_ELEMS = kTK * VS;
   static constexpr int BUF = K_ELEMS + V_ELEMS;    // one stage, bf16 elements
-  static constexpr int KCHUNKS = kTK * D / 8;      // 16-byte chunks of a K tile
-  static constexpr int KITER = (KCHUNKS + kThreads - 1) / kThreads;
-  static constexpr int VTASKS = (kTK / 4) * (D / 8);  // 4 keys x 8 dims per task
-  static constexpr int VITER = (VTASKS + kThreads - 1) / kThreads;
+  static constexpr int CHUNKS = kTK * D / 8;       // 16-byte chunks of a K (or V) tile
 };
 
-__device__ __forceinline__ int vperm_pos(int k0) {
-  // position of the 4-key group starting at k0 (k0 % 4 == 0) inside V^T rows
-  int chunk = k0 >> 4, grp = (k0 >> 2) & 3;
-  int ng = (grp == 1) ? 2 : (grp == 2 ? 1 : grp);
-  return chunk * 16 + ng * 4;
-}
-
-template <int D>
+template <int D, int NT>
 struct KVRegs {
-  u32x4 k[BfTile<D>::KITER];
-  u32x4 v[BfTile<D>::VITER][4];
+  static constexpr int IT = (BfTile<D>::CHUNKS + NT - 1) / NT;
+  static constexpr bool EXACT = BfTile<D>::CHUNKS % NT == 0;
+  u32x4 k[IT];
+  u32x4 v[IT];
 };
 
-template <int D>
-__device__ __forceinline__ void load_kv_tile(KVRegs<D>& r, const uint16_t* __restrict__ kp,
+// Global -> registers without branches: key rows past kv_len re-read the last
+// row. Those keys are masked to -inf before the softmax (their weight is 0),
+// so what they hold never reaches the output.
+template <int D, int NT>
+__device__ __forceinline__ void load_kv_tile(KVRegs<D, NT>& r, const uint16_t* __restrict__ kp,
                                              const uint16_t* __restrict__ vp, int64_t row_stride,
                                              int key0, int kv_len, int tid) {
-  using T = BfTile<D>;
+  using R = KVRegs<D, NT>;
 #pragma unroll
-  for (int it = 0; it < T::KITER; ++it) {
-    int c = tid + it * kThreads;
-    int key = c / (D / 8), dc = c % (D / 8);
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (c < T::KCHUNKS && key0 + key < kv_len)
-      x = *reinterpret_cast<const u32x4*>(kp + (int64_t)(key0 + key) * row_stride + dc * 8);
-    r.k[it] = x;
-  }
-#pragma unroll
-  for (int it = 0; it < T::VITER; ++it) {
-    int c = tid + it * kThreads;
-    int kg = c % (kTK / 4), dc = c / (kTK / 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int key = key0 + kg * 4 + i;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (c < T::VTASKS && key < kv_len)
-        x = *reinterpret_cast<const u32x4*>(vp + (int64_t)key * row_stride + dc * 8);
-      r.v[it][i] = x;
+  for (int it = 0; it < R::IT; ++it) {
+    const int c = tid + it * NT;
+    if (R::EXACT || c < BfTile<D>::CHUNKS) {
+      const int key = min(key0 + c / (D / 8), kv_len - 1);
+      const int64_t off = (int64_t)key * row_stride + (c % (D / 8)) * 8;
+      r.k[it] = *reinterpret_cast<const u32x4*>(kp + off);
+      r.v[it] = *reinterpret_cast<const u32x4*>(vp + off);
     }
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_kv_tile(const KVRegs<D>& r, uint16_t* sbuf, int tid) {
+template <int D, int NT>
+__device__ __forceinline__ void store_kv_tile(const KVRegs<D, NT>& r, uint16_t* sbuf, int tid) {
   using T = BfTile<D>;
-  uint16_t* sK = sbuf;
-  uint16_t* sV = sbuf + T::K_ELEMS;
+  using R = KVRegs<D, NT>;
 #pragma unroll
-  for (int it = 0; it < T::KITER; ++it) {
-    int c = tid + it * kThreads;
-    if (c < T::KCHUNKS) {
-      int key = c / (D / 8), dc = c % (D / 8);
-      *reinterpret_cast<u32x4*>(sK + key * T::KS + dc * 8) = r.k[it];
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < T::VITER; ++it) {
-    int c = tid + it * kThreads;
-    if (c < T::VTASKS) {
-      int kg = c % (kTK / 4), dc = c / (kTK / 4);
-      int pos = vperm_pos(kg * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t a0 = r.v[it][0][e], a1 = r.v[it][1][e], a2 = r.v[it][2][e], a3 = r.v[it][3][e];
-        u32x2 lo, hi;  // dims 2e and 2e+1, keys kg*4 .. kg*4+3
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(sV + (dc * 8 + 2 * e) * T::VS + pos) = lo;
-        *reinterpret_cast<u32x2*>(sV + (dc * 8 + 2 * e + 1) * T::VS + pos) = hi;
-      }
+  for (int it = 0; it < R::IT; ++it) {
+    const int c = tid + it * NT;
+    if (R::EXACT || c < T::CHUNKS) {
+      const int key = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(sbuf + key * T::KS + col) = r.k[it];
+      *reinterpret_cast<u32x4*>(sbuf + T::K_ELEMS + key * T::VS + col) = r.v[it];
     }
   }
 }
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_mfma(AttnParams p) {
+__device__ __forceinline__ float max_xor32(float x) {
+  // max with the value held by lane L^32 (one lane swap across the wave halves)
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   using T = BfTile<D>;
-  constexpr int ROWS = 128 * QB;
+  constexpr int NT = NW * 64;
+  constexpr int ROWS = 32 * NW;
   constexpr int KSTEPS = D / 16;
   constexpr int KB = kTK / 32;   // 32-key blocks per tile
   constexpr int KC = kTK / 16;   // 16-key chunks per tile
@@ -203,158 +197,140 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_mfma(AttnParams p) {
   const uint16_t* __restrict__ vg =
       reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.kv_bstride + (int64_t)g * D;
 
-  // rows of this lane (one per query block)
-  int row_a[QB], row_h[QB];
-  bool row_ok[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    int rho = rho0 + wave * 32 * QB + qb * 32 + col;
-    row_ok[qb] = rho < rows_total;
-    int rr = row_ok[qb] ? rho : rows_total - 1;
-    row_a[qb] = rr / p.group;
-    row_h[qb] = g * p.group + (rr - row_a[qb] * p.group);
-  }
+  // this lane's query row
+  const int rho = rho0 + wave * 32 + col;
+  const bool row_ok = rho < rows_total;
+  const int rr = row_ok ? rho : rows_total - 1;
+  const int row_a = rr / p.group;
+  const int row_h = g * p.group + (rr - row_a * p.group);
+  // last key index visible to this row (keys past kv_len are never visible)
+  const int lim = geom.kind == kAllVisible ? p.kv_len - 1
+                : (geom.kind == kNoneVisible ? -1 : min(row_a - geom.delta, p.kv_len - 1));
 
   // Q^T fragments (B operand): lane holds dims 16t + 8*half .. +8 of its row
-  bf16x8 qf[QB][KSTEPS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const uint16_t* qrow = qg + ((int64_t)row_a[qb] * p.hq + row_h[qb]) * D + 8 * half;
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t* qrow = qg + ((int64_t)row_a * p.hq + row_h) * D + 8 * half;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok[qb]) x = *reinterpret_cast<const u32x4*>(qrow + 16 * t);
-      qf[qb][t] = __builtin_bit_cast(bf16x8, x);
+      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * t);
+      if (!row_ok) x = u32x4{0u, 0u, 0u, 0u};
+      qf[t] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  f32x16 oacc[QB][DB];
-  float m_run[QB], l_run[QB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = kNegInf;
-    l_run[qb] = 0.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
-  }
-
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
   const float sl2 = p.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // per-lane offsets of the two LDS operand reads
+  const int k_lane = col * T::KS + 8 * half;
+  const int grp = lane >> 4, sl = lane & 15;
+  const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * T::VS + 16 * (grp & 1) + 4 * (sl & 3);
 
   if (n_kt > 0) {
-    KVRegs<D> regs;
-    load_kv_tile<D>(regs, kg, vg, kv_row_stride, 0, p.kv_len, tid);
-    store_kv_tile<D>(regs, smem, tid);
+    KVRegs<D, NT> regs;
+    load_kv_tile<D, NT>(regs, kg, vg, kv_row_stride, 0, p.kv_len, tid);
+    store_kv_tile<D, NT>(regs, smem, tid);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
       const uint16_t* sbuf = smem + (kt & 1) * T::BUF;
       const bool have_next = kt + 1 < n_kt;
-      if (have_next) load_kv_tile<D>(regs, kg, vg, kv_row_stride, (kt + 1) * kTK, p.kv_len, tid);
+      if (have_next) load_kv_tile<D, NT>(regs, kg, vg, kv_row_stride, (kt + 1) * kTK, p.kv_len, tid);
 
       // ---- S^T = K Q^T --------------------------------------------------
-      f32x16 s[KB][QB];
+      f32x16 s[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
-      const uint16_t* sK = sbuf;
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (kb * 32 + col) * T::KS + 16 * t + 8 * half);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][t], s[kb][qb], 0, 0, 0);
+          bf16x8 a = *reinterpret_cast<const bf16x8*>(sbuf + k_lane + kb * 32 * T::KS + 16 * t);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
         }
       }
 
-      // ---- mask (only tiles crossing the diagonal or the ragged tail) ----
+      // ---- mask (tiles crossing the diagonal or the ragged tail) --------
       const int key0 = kt * kTK;
       if (key0 + kTK > full_end) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-              bool vis = key < p.kv_len && visible(geom, row_a[qb], key);
-              if (!vis) s[kb][qb][i] = kNegInf;
-            }
-      }
-
-      // ---- online softmax (exp2 domain) --------------------------------
-      bf16x8 pf[QB][KC];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mt = kNegInf;
+        const int rel = lim - key0 - 4 * half;  // visible iff 8*(i/4) + i%4 + 32*kb <= rel
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][qb][i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run[qb], mt * sl2);
-        const float base = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - base);
-        m_run[qb] = m_new;
-        float ls = 0.f;
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + 8 * (i >> 2) + (i & 3) > rel) s[kb][i] = kNegInf;
+      }
+
+      // ---- online softmax (exp2 domain) --------------------------------
+      float mt = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          f32x16 pv;
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float e = fast_exp2(__builtin_fmaf(s[kb][qb][i], sl2, -base));
-            pv[i] = e;
-            ls += e;
-          }
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+      mt = max_xor32(mt);
+      const float m_new = fmaxf(m_run, mt * sl2);
+      const float base = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - base);
+      m_run = m_new;
+      bf16x8 pf[KC];
+      float ls = 0.f;
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            f32x8 h8;
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) h8[j] = pv[8 * c2 + j];
-            pf[qb][kb * 2 + c2] = __builtin_convertvector(h8, bf16x8);
-          }
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x8 e8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e8[j] = fast_exp2(__builtin_fmaf(s[kb][8 * c2 + j], sl2, -base));
+          const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
+          pf[kb * 2 + c2] = pb;
+          // row sum of the rounded weights (the same ones the numerator uses)
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, ls, false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, ls, false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, ls, false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, ls, false);
         }
-        l_run[qb] = alpha * l_run[qb] + ls;
-        if (!__all(alpha == 1.0f)) {
+      }
+      l_run = alpha * l_run + ls;
+      if (!__all(alpha == 1.0f)) {
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
-        }
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
 
       // ---- O^T += V^T P^T ------------------------------------------------
-      const uint16_t* sV = sbuf + T::K_ELEMS;
+      const uint16_t* sV = sbuf + T::K_ELEMS + v_lane;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + (db * 32 + col) * T::VS + c * 16 + 8 * half);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][c], oacc[qb][db], 0, 0, 0);
+          const s16x4 lo = lds_read_tr16(sV + (c * 16) * T::VS + db * 32);
+          const s16x4 hi = lds_read_tr16(sV + (c * 16 + 8) * T::VS + db * 32);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], oacc[db], 0, 0, 0);
         }
       }
 
-      if (have_next) store_kv_tile<D>(regs, smem + ((kt + 1) & 1) * T::BUF, tid);
+      if (have_next) store_kv_tile<D, NT>(regs, smem + ((kt + 1) & 1) * T::BUF, tid);
       __syncthreads();
     }
   }
 
   // ---- epilogue: (m, l, acc) with m in natural units --------------------
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    if (!row_ok[qb]) continue;
-    const int64_t r = ((int64_t)b * p.q_len + row_a[qb]) * p.hq + row_h[qb];
+  const float lt = sum_xor32(l_run);
+  if (row_ok) {
+    const int64_t r = ((int64_t)b * p.q_len + row_a) * p.hq + row_h;
     if (half == 0) {
-      p.m[r] = (m_run[qb] == kNegInf) ? kNegInf : m_run[qb] * kLn2;
+      p.m[r] = (m_run == kNegInf) ? kNegInf : m_run * kLn2;
       p.l[r] = lt;
     }
     float* arow = p.acc + r * D;
@@ -362,10 +338,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_mfma(AttnParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        int d = db * 32 + 8 * u + 4 * half;
+        const int d = db * 32 + 8 * u + 4 * half;
         if (d < D) {
-          f32x4 o = {oacc[qb][db][4 * u], oacc[qb][db][4 * u + 1], oacc[qb][db][4 * u + 2],
-                     oacc[qb][db][4 * u + 3]};
+          f32x4 o = {oacc[db][4 * u], oacc[db][4 * u + 1], oacc[db][4 * u + 2], oacc[db][4 * u + 3]};
           *reinterpret_cast<f32x4*>(arow + d) = o;
         }
       }
@@ -563,12 +538,12 @@ static int grid_for(int64_t total_threads) {
   return (int)blocks;
 }
 
-template <int D, int QB>
+template <int D, int NW>
 static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
-  constexpr int ROWS = 128 * QB;
+  constexpr int ROWS = 32 * NW;
   p.n_row_tiles = (p.rows_per_bg + ROWS - 1) / ROWS;
   const size_t smem = 2 * BfTile<D>::BUF * sizeof(uint16_t);
-  auto kern = attn_bf16_mfma<D, QB>;
+  auto kern = attn_bf16_mfma<D, NW>;
   static bool attr_set = false;  // per instantiation; benign race (idempotent)
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -577,7 +552,7 @@ static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
     attr_set = true;
   }
   const int64_t grid = (int64_t)p.batch * p.hkv * p.n_row_tiles;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), smem, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), smem, stream, p);
   return hipGetLastError();
 }
 
@@ -591,23 +566,21 @@ static hipError_t launch_f32(AttnParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int bf16_rows_per_wg(int qb) { return 128 * qb; }
-
-hipError_t launch_attention(const AttnParams& p, int is_bf16, int qb, hipStream_t stream) {
+hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream) {
   if (is_bf16) {
-    if (qb == 2) {
+    if (waves == 4) {
       switch (p.head_dim) {
-        case 16: return launch_bf16<16, 2>(p, stream);
-        case 32: return launch_bf16<32, 2>(p, stream);
-        case 64: return launch_bf16<64, 2>(p, stream);
-        case 128: return launch_bf16<128, 2>(p, stream);
+        case 16: return launch_bf16<16, 4>(p, stream);
+        case 32: return launch_bf16<32, 4>(p, stream);
+        case 64: return launch_bf16<64, 4>(p, stream);
+        case 128: return launch_bf16<128, 4>(p, stream);
       }
     } else {
       switch (p.head_dim) {
-        case 16: return launch_bf16<16, 1>(p, stream);
-        case 32: return launch_bf16<32, 1>(p, stream);
-        case 64: return launch_bf16<64, 1>(p, stream);
-        case 128: return launch_bf16<128, 1>(p, stream);
+        case 16: return launch_bf16<16, 8>(p, stream);
+        case 32: return launch_bf16<32, 8>(p, stream);
+        case 64: return launch_bf16<64, 8>(p, stream);
+        case 128: return launch_bf16<128, 8>(p, stream);
       }
     }
   } else {

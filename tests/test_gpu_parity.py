@@ -118,7 +118,11 @@ def test_block_partial_matches_oracle(dtype, d, hq, hkv, blen, n, layout, causal
             assert np.all(gacc[empty] == 0)
             ok = ~empty
             assert np.abs(gm[ok] - rm[ok]).max(initial=0) <= 1e-5 * np.maximum(1, np.abs(rm[ok])).max(initial=1)
-            assert np.abs(gl[ok] / rl[ok] - 1).max(initial=0) <= 1e-4
+            # bf16: l sums the bf16-rounded weights that also form acc (each weight
+            # carries at most 2^-9 relative rounding), so l matches to ~4e-3 while
+            # acc / l stays a convex combination of V with those same weights.
+            l_tol = 1e-4 if dtype == torch.float32 else 4e-3
+            assert np.abs(gl[ok] / rl[ok] - 1).max(initial=0) <= l_tol
             o_g = gacc[ok] / gl[ok][:, None]
             o_r = racc[ok] / rl[ok][:, None]
             assert np.abs(o_g - o_r).max(initial=0) <= tol
