@@ -20,7 +20,6 @@ workload (a reported baseline, not a target).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,24 +32,15 @@ sys.path.insert(0, ROOT)
 
 from ring_attention_blockwise_ra_amd import binding as B  # noqa: E402
 from ring_attention_blockwise_ra_amd import synth, workloads  # noqa: E402
+from ring_attention_blockwise_ra_amd.profiling import kernel_source_hash  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
-KERNEL_SOURCES = ["ring_attention_blockwise_ra_amd/csrc/ra_kernels.hip",
-                  "ring_attention_blockwise_ra_amd/csrc/ra_sched.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_bf16_mfma_c4_counters.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def timed(fn, stream=None):
@@ -110,7 +100,7 @@ def block_pairs(layout, causal, n, r, j, blen):
     return blen * (blen + 1) // 2 if j <= r else blen * (blen - 1) // 2
 
 
-def overlap_leg(w, out, lse, ws, reps=2):
+def overlap_leg(w, out, lse, ws, reps=3):
     """T_ring (copies on a side stream), T_nocopy (same kernels reading the
     source blocks in place, through the public entry points), T_copy (the
     N-1 staging copies alone). efficiency = 1 - max(0, T_ring - T_nocopy)/T_copy."""
@@ -143,12 +133,16 @@ def overlap_leg(w, out, lse, ws, reps=2):
             stage_k.copy_(w["k"][j])
             stage_v.copy_(w["v"][j])
 
-    t_ring = min(timed(lambda: ring_call(w, out, lse, ws)) for _ in range(reps))
-    t_nocopy = min(timed(nocopy) for _ in range(reps))
+    tr, tn = [], []
+    for _ in range(reps):  # interleaved, so clock drift hits both alike
+        tr.append(timed(lambda: ring_call(w, out, lse, ws)))
+        tn.append(timed(nocopy))
+    t_ring, t_nocopy = sorted(tr)[len(tr) // 2], sorted(tn)[len(tn) // 2]
     t_copy = min(timed(copies) for _ in range(reps))
     eff = 1.0 - max(0.0, t_ring - t_nocopy) / t_copy if t_copy > 0 else 1.0
     return dict(efficiency=round(eff, 4), t_ring_ms=round(t_ring, 3),
                 t_nocopy_ms=round(t_nocopy, 3), t_copy_ms=round(t_copy, 3),
+                ring_spread_ms=round(max(tr) - min(tr), 3),
                 copy_bytes=int(2 * (n - 1) * w["k"][0].numel() * w["k"].element_size()))
 
 
@@ -223,6 +217,8 @@ def main():
     ap.add_argument("--layouts", default=None, help="comma list; default: the workload's")
     ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, one device copy of this size (counter calibration)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the timed steps (for profiler runs)")
     args = ap.parse_args()
@@ -260,6 +256,14 @@ def main():
         ws_list.append(w)
         torch.cuda.synchronize()
         log(f"[bench] prepared {layout} in {time.time() - t0:.1f}s")
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     def step():
         for w in ws_list:

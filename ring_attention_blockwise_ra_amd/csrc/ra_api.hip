@@ -82,6 +82,9 @@ ra_status validate_problem(const ra_problem* p, Shape* s) {
                 (long long)p->q_len, (long long)p->kv_len);
   if (isnan(p->scale) || isinf(p->scale))
     return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  // the kernels address one batch row of a KV block with 32-bit offsets
+  if ((int64_t)p->kv_len * p->hkv * p->head_dim > INT32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "kv_len*hkv*head_dim exceeds 2^31-1 elements");
   const int64_t group = p->hq / p->hkv;
   if (group * p->q_len > INT32_MAX)
     return fail(RA_ERR_INVALID_ARG, "(hq/hkv)*q_len exceeds 2^31-1");

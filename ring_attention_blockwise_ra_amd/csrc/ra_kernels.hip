@@ -34,6 +34,7 @@ namespace ra {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -41,6 +42,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// the exponent reference moves only when the running max passes it by more
+// than this (log2 units): weights stay <= 2^kRescale
+constexpr float kRescale = 8.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -76,63 +80,26 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // V[k0 .. k0+3][d0 + i]: four consecutive keys of one head dimension.
 
 constexpr int kThreads = 256;  // workgroup size of the fp32 and elementwise kernels
-constexpr int kTK = 64;
+constexpr int kTK = 64;        // keys per tile
+constexpr int kSlots = 4;      // LDS ring of K/V tiles; loads run kSlots-1 tiles ahead
 
+// LDS layout of one K or V tile: 64 rows (keys) of D bf16, no padding. Each
+// 16-byte chunk c of row r is stored at chunk position c ^ f(r) with
+// f(r) = 2*(r%4) + (r/4)%2 (masked to the chunks of a row). With that swizzle
+// the 16-byte K operand reads (8 rows, one chunk) and the transposed V reads
+// (4 rows, two adjacent chunks) each touch every bank once.
 template <int D>
 struct BfTile {
   static constexpr int DP = D < 32 ? 32 : D;       // head dims padded to the MFMA M of 32
-  static constexpr int KS = D + 8;                 // K row stride (bf16): 16-byte reads
-                                                   // of 8 rows hit distinct banks
-  static constexpr int VS = DP + 16;               // V row stride (bf16): the 4 rows of a
-                                                   // transposed read hit distinct banks
-  static constexpr int K_ELEMS = kTK * KS;
-  static constexpr int V_ELEMS = kTK * VS;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;    // one stage, bf16 elements
-  static constexpr int CHUNKS = kTK * D / 8;       // 16-byte chunks of a K (or V) tile
+  static constexpr int ROWB = D * 2;               // bytes per key row
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int TB = kTK * ROWB;            // bytes per K (or V) tile
+  static constexpr int SLOT = 2 * TB;              // K tile then V tile
+  static constexpr int SEGS = TB / 1024;           // 1 KiB DMA segments per tile
+  static constexpr int ROWS_PER_SEG = 1024 / ROWB;
 };
 
-template <int D, int NT>
-struct KVRegs {
-  static constexpr int IT = (BfTile<D>::CHUNKS + NT - 1) / NT;
-  static constexpr bool EXACT = BfTile<D>::CHUNKS % NT == 0;
-  u32x4 k[IT];
-  u32x4 v[IT];
-};
-
-// Global -> registers without branches: key rows past kv_len re-read the last
-// row. Those keys are masked to -inf before the softmax (their weight is 0),
-// so what they hold never reaches the output.
-template <int D, int NT>
-__device__ __forceinline__ void load_kv_tile(KVRegs<D, NT>& r, const uint16_t* __restrict__ kp,
-                                             const uint16_t* __restrict__ vp, int64_t row_stride,
-                                             int key0, int kv_len, int tid) {
-  using R = KVRegs<D, NT>;
-#pragma unroll
-  for (int it = 0; it < R::IT; ++it) {
-    const int c = tid + it * NT;
-    if (R::EXACT || c < BfTile<D>::CHUNKS) {
-      const int key = min(key0 + c / (D / 8), kv_len - 1);
-      const int64_t off = (int64_t)key * row_stride + (c % (D / 8)) * 8;
-      r.k[it] = *reinterpret_cast<const u32x4*>(kp + off);
-      r.v[it] = *reinterpret_cast<const u32x4*>(vp + off);
-    }
-  }
-}
-
-template <int D, int NT>
-__device__ __forceinline__ void store_kv_tile(const KVRegs<D, NT>& r, uint16_t* sbuf, int tid) {
-  using T = BfTile<D>;
-  using R = KVRegs<D, NT>;
-#pragma unroll
-  for (int it = 0; it < R::IT; ++it) {
-    const int c = tid + it * NT;
-    if (R::EXACT || c < T::CHUNKS) {
-      const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(sbuf + key * T::KS + col) = r.k[it];
-      *reinterpret_cast<u32x4*>(sbuf + T::K_ELEMS + key * T::VS + col) = r.v[it];
-    }
-  }
-}
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
 
 __device__ __forceinline__ float max_xor32(float x) {
   // max with the value held by lane L^32 (one lane swap across the wave halves)
@@ -147,23 +114,46 @@ __device__ __forceinline__ float sum_xor32(float x) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Direct global -> LDS copy of one K or V tile (global_load_lds_dwordx4: lane
+// l of an instruction writes bytes [16l, 16l+16) of a 1 KiB LDS segment and
+// reads any global address). Every wave issues LPW instructions, so the
+// per-wave count of outstanding loads is the same in all waves. Key rows past
+// kv_len re-read the last row; those keys are masked before the softmax.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int row_stride, int key0,
+                                         int kv_len, char* lds_tile, int wave, int lane) {
+  using T = BfTile<D>;
+  constexpr int LPW = T::SEGS >= NW ? T::SEGS / NW : 1;
+  const int rin = lane / T::CPR, pc = lane % T::CPR;
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int seg = (wave + j * NW) % T::SEGS;
+    const int row = seg * T::ROWS_PER_SEG + rin;
+    const int lc = pc ^ (swz(row) & (T::CPR - 1));
+    const int key = min(key0 + row, kv_len - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(src + key * row_stride + lc * 8),
+                                     (lds_void*)(lds_tile + seg * 1024), 16, 0, 0);
+  }
 }
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   using T = BfTile<D>;
-  constexpr int NT = NW * 64;
   constexpr int ROWS = 32 * NW;
   constexpr int KSTEPS = D / 16;
   constexpr int KB = kTK / 32;   // 32-key blocks per tile
   constexpr int KC = kTK / 16;   // 16-key chunks per tile
   constexpr int DB = T::DP / 32; // 32-dim blocks of the output
+  constexpr int LPW = T::SEGS >= NW ? T::SEGS / NW : 1;
+  constexpr int LOADS_PER_TILE = 2 * LPW;  // per wave: K and V
 
-  extern __shared__ __align__(16) uint16_t smem[];
+  extern __shared__ __align__(16) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   const int n_kt = (key_end + kTK - 1) / kTK;
 
   const uint16_t* __restrict__ qg = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bstride;
-  const int64_t kv_row_stride = (int64_t)p.hkv * D;
+  const int kv_row_stride = p.hkv * D;
   const uint16_t* __restrict__ kg =
       reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.kv_bstride + (int64_t)g * D;
   const uint16_t* __restrict__ vg =
@@ -228,101 +218,174 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   const float sl2 = p.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // per-lane offsets of the two LDS operand reads
-  const int k_lane = col * T::KS + 8 * half;
-  const int grp = lane >> 4, sl = lane & 15;
-  const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * T::VS + 16 * (grp & 1) + 4 * (sl & 3);
+  // Per-lane byte offsets of the LDS operand reads (swizzled chunk positions).
+  // K operand, step t = 4u + w: row col (+32 kb), chunk 2t + half.
+  int koff[4];
+  {
+    const int fr = swz(col) & (T::CPR - 1);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) koff[w] = col * T::ROWB + (((2 * w + half) ^ fr) & (T::CPR - 1)) * 16;
+  }
+  // V^T operand (transposed reads): row 4*(grp/2) + sl/4 (+16 c16 + 8 cc),
+  // head dims db*32 + 16*(grp%2) + 4*(sl%4) .. +3.
+  int voff[2];
+  {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int r = 4 * (grp >> 1) + (sl >> 2);
+    const int fr = swz(r) & (T::CPR - 1);
+    const int lowc = 2 * (grp & 1) + ((sl >> 1) & 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      voff[x] = r * T::ROWB + (((4 * x + lowc) & (T::CPR - 1)) ^ fr) * 16 + 8 * (sl & 1);
+  }
+
+  // Lazy rescaling: P, l and O are kept relative to a per-row reference
+  // `base` (log2 units) that only moves when the running max m_run exceeds
+  // it by more than kRescale; the epilogue converts to the exact max. This
+  // keeps the O rescale (a multiply per accumulator) off most units.
+  float base = kNegInf;
+
+  auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT; };
+  auto slot_v = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT + T::TB; };
+  auto issue = [&](int t) {
+    dma_tile<D, NW>(kg, kv_row_stride, t * kTK, p.kv_len, slot_k(t), wave, lane);
+    dma_tile<D, NW>(vg, kv_row_stride, t * kTK, p.kv_len, slot_v(t), wave, lane);
+  };
+  // Work is done in units of 32 keys: unit u is half u%2 of tile u/2. S(u)
+  // is one 32x32 MFMA tile (16 registers per lane), P(u) two bf16x8 operands.
+  auto qk = [&](f32x16& s_out, int u) {
+    const char* sK = slot_k(u >> 1) + (u & 1) * 32 * T::ROWB;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + koff[t & 3] + (t >> 2) * 128);
+      s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? f32x16{} : s_out, 0, 0, 0);
+    }
+  };
+  auto pv = [&](const bf16x8 (&pf)[2], int u) {
+    const char* sV = slot_v(u >> 1) + (u & 1) * 32 * T::ROWB;
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int db = j >> 1, c = j & 1;
+      const char* a0 = sV + voff[db & 1] + (db >> 1) * 128 + (c * 16) * T::ROWB;
+      const s16x4 lo = lds_read_tr16(a0);
+      const s16x4 hi = lds_read_tr16(a0 + 8 * T::ROWB);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], oacc[db], 0, 0, 0);
+    }
+  };
+  // mask S(u) past the diagonal or the ragged tail, then move the reference
+  // with its row max; returns the factor O must take after the PV of P(u-1)
+  auto mask_and_ref = [&](f32x16& sc, int u) -> float {
+    const int key0 = u * 32;
+    if (key0 + 32 > full_end) {
+      const int rel = lim - key0 - 4 * half;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (8 * (q >> 2) + (q & 3) > rel) sc[q] = kNegInf;
+    }
+    float mt = kNegInf;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mt = fmaxf(mt, sc[q]);
+    m_run = fmaxf(m_run, max_xor32(mt) * sl2);
+    const bool move = m_run > base + kRescale;
+    const float nb = move ? m_run : base;
+    const float alpha = move ? fast_exp2(base - nb) : 1.0f;  // 0 when base was -inf
+    base = nb;
+    l_run *= alpha;
+    return alpha;
+  };
+  // P(u) = exp2(S(u) c - base) as bf16 operands; l += sum of the rounded
+  // weights (the same ones the numerator uses)
+  auto softmax_p = [&](const f32x16& sc, bf16x8 (&pf)[2]) {
+    const float bexp = base == kNegInf ? 0.f : base;
+    float ls = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f32x8 e8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e8[q] = fast_exp2(__builtin_fmaf(sc[8 * c + q], sl2, -bexp));
+      const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
+      pf[c] = pb;
+#pragma unroll
+      for (int o = 0; o < 8; o += 2)
+        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[o], pb[o + 1]}, ones, ls, false);
+    }
+    l_run += ls;
+  };
+  auto rescale_o = [&](float alpha) {
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+  };
+  // One unit u of the three-stage pipeline: with S(u) complete and P(u-1)
+  // pending, issue S(u+1) = K(u+1) Q^T, compute P(u), and issue
+  // O += V(u-1) P(u-1). None of these MFMAs depends on the exponentials of
+  // the same unit, so the matrix core and the transcendental unit overlap.
+  auto unit = [&](f32x16& sc, f32x16& sn, const bf16x8 (&pprev)[2], bf16x8 (&pcur)[2], int u,
+                  bool has_next, bool has_prev) {
+    const float alpha = mask_and_ref(sc, u);
+    if (has_next) qk(sn, u + 1);
+    softmax_p(sc, pcur);
+    if (has_prev) pv(pprev, u - 1);
+    rescale_o(alpha);
+  };
 
   if (n_kt > 0) {
-    KVRegs<D, NT> regs;
-    load_kv_tile<D, NT>(regs, kg, vg, kv_row_stride, 0, p.kv_len, tid);
-    store_kv_tile<D, NT>(regs, smem, tid);
-    __syncthreads();
+    // Pipeline. Tiles live in a ring of kSlots LDS slots. Tile step t runs
+    // units 2t+1 and 2t+2, which read K only from tile t+1 and V only from
+    // tile t; it first issues the DMA of tile t+3 into the slot of tile t-1
+    // (whose last reader, the V of unit 2t, finished before the barrier that
+    // ended step t-1), and before its closing barrier each wave waits until
+    // at most one tile of its own loads (tile t+3) is in flight, i.e. tile
+    // t+2 has landed. Tiles past the last one are loaded (clamped rows) but
+    // never read, which keeps every wave's load count uniform.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q fragments
+    issue(0);
+    issue(1);
+    issue(2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const uint16_t* sbuf = smem + (kt & 1) * T::BUF;
-      const bool have_next = kt + 1 < n_kt;
-      if (have_next) load_kv_tile<D, NT>(regs, kg, vg, kv_row_stride, (kt + 1) * kTK, p.kv_len, tid);
-
-      // ---- S^T = K Q^T --------------------------------------------------
-      f32x16 s[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          bf16x8 a = *reinterpret_cast<const bf16x8*>(sbuf + k_lane + kb * 32 * T::KS + 16 * t);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
-        }
-      }
-
-      // ---- mask (tiles crossing the diagonal or the ragged tail) --------
-      const int key0 = kt * kTK;
-      if (key0 + kTK > full_end) {
-        const int rel = lim - key0 - 4 * half;  // visible iff 8*(i/4) + i%4 + 32*kb <= rel
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + 8 * (i >> 2) + (i & 3) > rel) s[kb][i] = kNegInf;
-      }
-
-      // ---- online softmax (exp2 domain) --------------------------------
-      float mt = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-      mt = max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt * sl2);
-      const float base = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
-      m_run = m_new;
-      bf16x8 pf[KC];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          f32x8 e8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) e8[j] = fast_exp2(__builtin_fmaf(s[kb][8 * c2 + j], sl2, -base));
-          const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
-          pf[kb * 2 + c2] = pb;
-          // row sum of the rounded weights (the same ones the numerator uses)
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, ls, false);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, ls, false);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, ls, false);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, ls, false);
-        }
-      }
-      l_run = alpha * l_run + ls;
-      if (!__all(alpha == 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T ------------------------------------------------
-      const uint16_t* sV = sbuf + T::K_ELEMS + v_lane;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const s16x4 lo = lds_read_tr16(sV + (c * 16) * T::VS + db * 32);
-          const s16x4 hi = lds_read_tr16(sV + (c * 16 + 8) * T::VS + db * 32);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], oacc[db], 0, 0, 0);
-        }
-      }
-
-      if (have_next) store_kv_tile<D, NT>(regs, smem + ((kt + 1) & 1) * T::BUF, tid);
-      __syncthreads();
+    const int n_u = (key_end + 31) / 32;  // units with any visible key
+    f32x16 sA, sB;
+    bf16x8 pA[2], pB[2];
+    qk(sA, 0);
+    unit(sA, sB, pB, pA, 0, n_u > 1, false);  // S(1) -> sB, P(0) -> pA
+    int t = 0;
+    for (; 2 * t + 3 < n_u; ++t) {
+      issue(t + 3);
+      unit(sB, sA, pA, pB, 2 * t + 1, true, true);  // S(2t+2) -> sA, P(2t+1) -> pB
+      unit(sA, sB, pB, pA, 2 * t + 2, true, true);  // S(2t+3) -> sB, P(2t+2) -> pA
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
     }
+    // tail: units 2t+1 .. n_u-1 (at most two); every tile they read has
+    // landed once this wave's loads are complete and all waves met
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    int u = 2 * t + 1;
+    if (u < n_u) {
+      unit(sB, sA, pA, pB, u, u + 1 < n_u, true);
+      ++u;
+      if (u < n_u) {
+        unit(sA, sB, pB, pA, u, false, true);
+        pv(pA, u);
+      } else {
+        pv(pB, u - 1);
+      }
+    } else {
+      pv(pA, u - 1);
+    }
+  }
+
+  // convert (l, O) from the reference `base` to the exact running max
+  if (base != kNegInf) {
+    const float f = fast_exp2(base - m_run);
+    l_run *= f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= f;
   }
 
   // ---- epilogue: (m, l, acc) with m in natural units --------------------
@@ -542,7 +605,7 @@ template <int D, int NW>
 static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
   constexpr int ROWS = 32 * NW;
   p.n_row_tiles = (p.rows_per_bg + ROWS - 1) / ROWS;
-  const size_t smem = 2 * BfTile<D>::BUF * sizeof(uint16_t);
+  const size_t smem = kSlots * BfTile<D>::SLOT;  // ring of K/V tile slots
   auto kern = attn_bf16_mfma<D, NW>;
   static bool attr_set = false;  // per instantiation; benign race (idempotent)
   if (!attr_set) {

@@ -1,0 +1,128 @@
+"""Summaries of rocprofv3 output for the attention path.
+
+    python -m ring_attention_blockwise_ra_amd.profiling trace  <kernel_trace.csv> <kernel_stats.csv>
+    python -m ring_attention_blockwise_ra_amd.profiling traffic <fetch_dir> <write_dir> <out.json>
+
+trace:   per-kernel statistics of the attention, merge and finalize kernels,
+         and how much of the side-queue staging copy time ran while an
+         attention kernel was executing (the overlap of the staged ring).
+traffic: HBM bytes per attention launch from two counter runs (FETCH_SIZE,
+         then WRITE_SIZE; KiB per dispatch), each scaled by what the same
+         counter reads for the calibration copy of known size that bench.py
+         performs with --calib-copy-mib. Writes a JSON that bench.py reports
+         as roofline.traffic while the kernel source hash still matches.
+"""
+
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ATTN = "attn_bf16_mfma"
+COPY = "copyBuffer"
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ["ring_attention_blockwise_ra_amd/csrc/ra_kernels.hip",
+                  "ring_attention_blockwise_ra_amd/csrc/ra_sched.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def trace_summary(trace_csv: str, stats_csv: str) -> dict:
+    rows = _rows(trace_csv)
+    attn = [r for r in rows if ATTN in r["Kernel_Name"]]
+    attn_q = {r["Queue_Id"] for r in attn}
+    spans = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in attn)
+    # staging copies: blit-copy kernels on a queue the attention kernel does not use
+    copies = [r for r in rows if COPY in r["Kernel_Name"] and r["Queue_Id"] not in attn_q]
+    tot = hidden = 0
+    for r in copies:
+        s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        tot += e - s
+        o = sum(max(0, min(e, b) - max(s, a)) for a, b in spans)
+        hidden += min(o, e - s)
+    stats = {}
+    for r in _rows(stats_csv):
+        name = r["Name"]
+        for key in ("attn_bf16_mfma", "attn_f32_fma", "merge_partials", "finalize_kernel",
+                    "fill_empty", COPY):
+            if key in name:
+                stats[name[:80]] = dict(calls=int(r["Calls"]), avg_ms=float(r["AverageNs"]) / 1e6,
+                                        total_ms=float(r["TotalDurationNs"]) / 1e6,
+                                        pct=float(r["Percentage"]))
+    return dict(kernels=stats, staging_copies=len(copies), staging_copy_ms=tot / 1e6,
+                staging_copy_hidden_ms=hidden / 1e6,
+                staging_copy_hidden_frac=(hidden / tot) if tot else None)
+
+
+def _counter_values(run_dir: str, counter: str):
+    """{dispatch_id: (kernel_name, value)} from a --pmc csv directory."""
+    out = {}
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {run_dir}")
+    for path in files:
+        for r in _rows(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            val = float(r["Counter_Value"])
+            name = r.get("Kernel_Name", "")
+            if did in out:  # several rows per dispatch (per XCD / instance): sum
+                out[did] = (name, out[did][1] + val)
+            else:
+                out[did] = (name, val)
+    return out
+
+
+def traffic(fetch_dir: str, write_dir: str, calib_bytes: int) -> dict:
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = _counter_values(d, counter)
+        copies = [v for n, v in vals.values() if COPY in n]
+        if not copies:
+            raise RuntimeError(f"{counter}: no calibration copy dispatch found")
+        calib_kib = max(copies)  # the calibration copy is the largest copy dispatch
+        factor = calib_bytes / (calib_kib * 1024.0)
+        attn = [v for n, v in vals.values() if ATTN in n]
+        per_launch = sum(attn) / len(attn) * 1024.0 * factor
+        res[counter] = dict(calib_kib=calib_kib, factor=factor, launches=len(attn),
+                            bytes_per_launch=per_launch)
+    res["hbm_bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + \
+        res["WRITE_SIZE"]["bytes_per_launch"]
+    return res
+
+
+def main(argv):
+    if len(argv) >= 3 and argv[0] == "trace":
+        print(json.dumps(trace_summary(argv[1], argv[2]), indent=1))
+    elif len(argv) >= 4 and argv[0] == "traffic":
+        calib = int(argv[4]) if len(argv) > 4 else 1 << 30
+        t = traffic(argv[1], argv[2], calib)
+        t["kernel_source_hash"] = kernel_source_hash()
+        with open(argv[3], "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
