@@ -335,7 +335,7 @@ def main():
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_bf16_mfma<128,1>" if c["dtype"] == "bf16" else "attn_f32_fma",
+            "kernel": "attn_bf16_mfma<128,8>" if c["dtype"] == "bf16" else "attn_f32_fma",
             "launches": nl, "avg_launch_ms": round(km / max(nl, 1), 3),
             "flops_per_launch_avg": kf / max(nl, 1),
             "kernel_source_hash": src_hash,
