@@ -346,8 +346,29 @@ def main():
         ov = {w["layout"]: overlap_leg(w, w["out"], w["lse"], w["ws"]) for w in ws_list}
         tot = {k: sum(o[k] for o in ov.values()) for k in ("t_ring_ms", "t_nocopy_ms", "t_copy_ms")}
         eff = 1.0 - max(0.0, tot["t_ring_ms"] - tot["t_nocopy_ms"]) / tot["t_copy_ms"]
-        result["overlap"] = dict(efficiency=round(eff, 4), **{k: round(v, 3) for k, v in tot.items()},
-                                 per_layout=ov)
+        # On the 1M-token share the copies (~3 ms) are below the run-to-run
+        # spread of a ~3 s ring, so this timing difference is noise; the
+        # kernel trace (profiling.py trace) measures that case directly. The
+        # same timing method is resolved on the 8192-token workload, whose
+        # steps are tens of microseconds and whose copies are a visible share.
+        result["overlap"] = dict(efficiency_timing=round(eff, 4),
+                                 **{k: round(v, 3) for k, v in tot.items()}, per_layout=ov,
+                                 note="timing difference below run-to-run spread; see "
+                                      "small_workload and the kernel-trace figure")
+        if args.workload != "c2":
+            w2 = workloads.prepare("c2", "contiguous", 7, device=dev)
+            b2, lq2, hq2, d2 = w2["q"].shape
+            prob2 = B.make_problem(dtype=w2["q"].dtype, batch=b2, hq=hq2, hkv=w2["k"].shape[3],
+                                   head_dim=d2, q_len=lq2, kv_len=w2["k"].shape[2], n_ring=8,
+                                   rank=7, causal=True, layout="contiguous")
+            out2 = torch.empty(b2, lq2, hq2, d2, dtype=torch.float32, device=dev)
+            lse2 = torch.empty(b2, lq2, hq2, dtype=torch.float32, device=dev)
+            ws2 = torch.empty(B.ra_ring_workspace_bytes(prob2), dtype=torch.uint8, device=dev)
+            ring_call(w2, out2, lse2, ws2)
+            result["overlap"]["small_workload"] = dict(
+                workload="c2: 8192 tokens, N=8 blocks of 1024, causal contiguous, rank 7",
+                **overlap_leg(w2, out2, lse2, ws2, reps=41))
+            del w2, out2, lse2, ws2
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
         log("[bench] merge leg done")
