@@ -23,9 +23,13 @@ Pages cited (by title and section; the pages are web text on Ring Attention):
        processing flow (step t uses the block received at step t-1) and on
        communication/compute overlap.
   [AU] AI Understanding, "Sekvensparallellism och ringuppmarksamhet": sections
-       "Djupdykning" (each device owns a contiguous chunk of tokens) and
+       "Djupdykning" (each device owns a contiguous chunk of tokens),
        "Teknisk insikt" (online softmax makes blockwise equal to full
-       attention).
+       attention) and "Framtiden for sekvensparallellism och
+       ringuppmarksamhet" (striped and zigzag variants rebalance the work
+       that causal masking leaves uneven).
+  [TS] also, section "Trade-off thuc te" (practical trade-offs): balancing
+       sequences of different lengths is named as a difficulty.
 
 Conventions
   * Tensors are [batch, seq, heads, head_dim] (the shape convention of the
@@ -39,7 +43,17 @@ Conventions
   * Layouts: "contiguous" -- block i holds tokens [i*B, (i+1)*B) ([AU]
     "Djupdykning"); "striped" -- token t belongs to block t mod N at local
     index floor(t / N) ([UL] closing remark: each device receives tokens
-    spread evenly over the sequence).
+    spread evenly over the sequence); "zigzag" -- the sequence is cut into
+    2N chunks of B/2 tokens and block i holds chunk i followed by chunk
+    2N-1-i ([AU] names zigzag as a rebalancing variant without defining it;
+    this pairing of an early with a late chunk is the plain reading, and it
+    gives every device the same causal work).
+  * Packed variable-length sequences ([TS] "Trade-off thuc te"): several
+    sequences of lengths L_s (each a multiple of N, of 2N for zigzag) are
+    concatenated; every sequence is split over the N blocks by the layout on
+    its own, and a block is the concatenation of its slices, sequence by
+    sequence. A key is visible to a query only inside the same sequence
+    (and, if causal, at a position within that sequence <= the query's).
   * A partial is (m, l, acc): m = max visible scaled score, l = sum of
     exp(s - m), acc = sum of exp(s - m) * v. A row with no visible key has
     the empty partial (-inf, 0, 0), which is the identity of the merge.
@@ -61,7 +75,7 @@ SKIP = 0
 PARTIAL = 1
 FULL = 2
 
-_LAYOUTS = ("contiguous", "striped")
+_LAYOUTS = ("contiguous", "striped", "zigzag")
 
 
 def _f64(x) -> np.ndarray:
@@ -86,14 +100,46 @@ def global_positions(layout: str, n_ring: int, block: int, block_len: int) -> np
     striped:    [UL] "How ring attention works", closing remark on striping --
                 tokens are spread evenly: token t -> block t mod N, local index
                 t // N, so position = a*N + block.
-    Pinned by tests: positions of all blocks partition range(N*B) exactly.
+    zigzag:     [AU] "Framtiden ..." -- chunks of h = block_len/2 tokens;
+                local a < h is chunk `block`, a >= h is chunk 2N-1-block:
+                position = c*h + (a mod h) for that chunk c.
+    Pinned by tests: positions of all blocks partition range(N*B) exactly;
+    local order is increasing in position; zigzag gives every rank the same
+    number of causal pairs.
     """
     if layout not in _LAYOUTS:
         raise ValueError(f"unknown layout {layout!r}")
     a = np.arange(block_len, dtype=np.int64)
     if layout == "contiguous":
         return block * block_len + a
-    return a * n_ring + block
+    if layout == "striped":
+        return a * n_ring + block
+    if block_len % 2:
+        raise ValueError("zigzag needs an even block length")
+    h = block_len // 2
+    chunk = np.where(a < h, block, 2 * n_ring - 1 - block)
+    return chunk * h + (a % h)
+
+
+def varlen_positions(layout: str, n_ring: int, block: int, seqlens):
+    """(sequence id, position within the sequence) of every token of ring
+    block `block` when sequences of lengths `seqlens` are packed: the block
+    holds, sequence after sequence, the L_s / N tokens the layout gives it
+    from each sequence ([TS] "Trade-off thuc te"; layouts as above).
+    Pinned by tests: over all blocks, the (id, position) pairs of each
+    sequence partition range(L_s)."""
+    ids, pos = [], []
+    for s, L in enumerate(seqlens):
+        L = int(L)
+        mult = 2 * n_ring if layout == "zigzag" else n_ring
+        if L % mult:
+            raise ValueError(f"sequence {s}: length {L} is not a multiple of {mult}")
+        b = L // n_ring
+        ids.append(np.full(b, s, dtype=np.int64))
+        pos.append(global_positions(layout, n_ring, block, b))
+    if not ids:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(ids), np.concatenate(pos)
 
 
 def ring_order(rank: int, n_ring: int) -> list[int]:
@@ -103,11 +149,17 @@ def ring_order(rank: int, n_ring: int) -> list[int]:
     return [(rank - s) % n_ring for s in range(n_ring)]
 
 
-def _visibility(q_pos: np.ndarray, k_pos: np.ndarray, causal: bool) -> np.ndarray:
-    """[Lq, Lk] boolean: key visible to query (causal: key pos <= query pos)."""
+def _visibility(q_pos: np.ndarray, k_pos: np.ndarray, causal: bool,
+                q_seq: np.ndarray | None = None, k_seq: np.ndarray | None = None) -> np.ndarray:
+    """[Lq, Lk] boolean: key visible to query (causal: key pos <= query pos;
+    packed sequences: also the same sequence id)."""
     if not causal:
-        return np.ones((q_pos.size, k_pos.size), dtype=bool)
-    return k_pos[None, :] <= q_pos[:, None]
+        vis = np.ones((q_pos.size, k_pos.size), dtype=bool)
+    else:
+        vis = k_pos[None, :] <= q_pos[:, None]
+    if q_seq is not None:
+        vis = vis & (k_seq[None, :] == q_seq[:, None])
+    return vis
 
 
 # --------------------------------------------------------------------------
@@ -171,6 +223,27 @@ def naive_attention_rows(q_rows, q_pos, k, v, causal: bool, scale: float | None 
     return out, lse
 
 
+def naive_attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float | None = None):
+    """O1 for packed sequences: plain attention of each sequence on its own.
+
+    q: [1, T, Hq, d]; k, v: [1, T, Hkv, d] in global packed order, sequence s
+    occupying tokens [cu_seqlens[s], cu_seqlens[s+1]). Returns (out, lse) of
+    shape [1, T, Hq, d] and [1, T, Hq].
+    Pinned by: torch CPU scaled_dot_product_attention with a block-diagonal
+    mask in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    out = np.zeros(q.shape)
+    lse = np.full(q.shape[:3], -np.inf)
+    cu = [int(x) for x in cu_seqlens]
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b > a:
+            o, l_ = naive_attention(q[:, a:b], k[:, a:b], v[:, a:b], causal, scale)
+            out[:, a:b], lse[:, a:b] = o, l_
+    return out, lse
+
+
 # --------------------------------------------------------------------------
 # O2 -- blockwise ring with online-softmax merge (separate code from O1).
 # --------------------------------------------------------------------------
@@ -182,7 +255,8 @@ def empty_partial(bsz: int, lq: int, hq: int, d: int):
     return (np.full((bsz, lq, hq), -np.inf), np.zeros((bsz, lq, hq)), np.zeros((bsz, lq, hq, d)))
 
 
-def block_partial(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = None):
+def block_partial(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = None,
+                  q_seq=None, k_seq=None):
     """Partial (m, l, acc) of the local queries against one arriving K/V block.
 
     [UL] "How ring attention works": each device keeps a running sum of the
@@ -192,7 +266,8 @@ def block_partial(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = Non
     acc = sum exp(s - m) v. A row with no visible key gets (-inf, 0, 0).
 
     q: [B, Lq, Hq, d] with positions q_pos [Lq]; k, v: [B, Lk, Hkv, d] with
-    positions k_pos [Lk].
+    positions k_pos [Lk]. q_seq, k_seq: sequence ids of packed sequences
+    (None: one sequence).
     Pinned by: m equals the exact max of visible scores and 1 <= l <= #visible
     (invariant); merged over all blocks equals O1 (brute force, SDPA).
     """
@@ -201,7 +276,9 @@ def block_partial(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = Non
     hkv = k.shape[2]
     if scale is None:
         scale = default_scale(d)
-    vis = _visibility(np.asarray(q_pos, np.int64), np.asarray(k_pos, np.int64), causal)
+    vis = _visibility(np.asarray(q_pos, np.int64), np.asarray(k_pos, np.int64), causal,
+                      None if q_seq is None else np.asarray(q_seq, np.int64),
+                      None if k_seq is None else np.asarray(k_seq, np.int64))
     has = vis.any(axis=1)
     m, l, acc = empty_partial(bsz, lq, hq, d)
     for b in range(bsz):
@@ -254,33 +331,43 @@ def finalize(state):
 
 
 def ring_state(q_share, k_blocks, v_blocks, rank: int, n_ring: int, layout: str,
-               causal: bool, scale: float | None = None, blocks=None, state=None):
+               causal: bool, scale: float | None = None, blocks=None, state=None,
+               seqlens=None):
     """Running (m, l, acc) after visiting `blocks` (default: the ring order of
     `rank`), starting from `state` (default: empty).
 
     q_share: [B, Lq, Hq, d] -- the local query block, fixed for the whole ring
     ([TS] "Y tuong cot loi"; [JS] ring structure). k_blocks, v_blocks:
     [N, B, Lk, Hkv, d] -- block j holds the tokens the layout gives to block j.
+    seqlens: lengths of packed sequences (batch 1), or None for one sequence
+    per batch row.
     Pinned by: the split-ring invariant (state after k steps merged with the
     rest equals the whole ring).
     """
     q_share = _f64(q_share)
     bsz, lq, hq, d = q_share.shape
-    q_pos = global_positions(layout, n_ring, rank, lq)
+    lk = k_blocks.shape[2]
+    if seqlens is None:
+        q_pos, q_seq = global_positions(layout, n_ring, rank, lq), None
+    else:
+        q_seq, q_pos = varlen_positions(layout, n_ring, rank, seqlens)
     if blocks is None:
         blocks = ring_order(rank, n_ring)
     if state is None:
         state = empty_partial(bsz, lq, hq, d)
-    lk = k_blocks.shape[2]
     for j in blocks:
-        k_pos = global_positions(layout, n_ring, j, lk)
-        part = block_partial(q_share, q_pos, k_blocks[j], v_blocks[j], k_pos, causal, scale)
+        if seqlens is None:
+            k_pos, k_seq = global_positions(layout, n_ring, j, lk), None
+        else:
+            k_seq, k_pos = varlen_positions(layout, n_ring, j, seqlens)
+        part = block_partial(q_share, q_pos, k_blocks[j], v_blocks[j], k_pos, causal, scale,
+                             q_seq, k_seq)
         state = merge_partials(state, part)
     return state
 
 
 def ring_share(q_share, k_blocks, v_blocks, rank: int, n_ring: int, layout: str,
-               causal: bool, scale: float | None = None, order=None):
+               causal: bool, scale: float | None = None, order=None, seqlens=None):
     """O2: one device's output after all N ring steps, (out, lse).
 
     Steps follow ring_order(rank) unless `order` (any permutation of the N
@@ -290,7 +377,7 @@ def ring_share(q_share, k_blocks, v_blocks, rank: int, n_ring: int, layout: str,
     tiny cases, arrival-order invariance, torch SDPA.
     """
     return finalize(ring_state(q_share, k_blocks, v_blocks, rank, n_ring, layout,
-                               causal, scale, blocks=order))
+                               causal, scale, blocks=order, seqlens=seqlens))
 
 
 def ring_share_literal(q_share, k_blocks, v_blocks, rank: int, n_ring: int,
@@ -322,7 +409,7 @@ def ring_share_literal(q_share, k_blocks, v_blocks, rank: int, n_ring: int,
 # --------------------------------------------------------------------------
 
 def tile_classes_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, j: int,
-                            q_len: int, kv_len: int, tq: int, tk: int) -> np.ndarray:
+                            q_len: int, kv_len: int, tq: int, tk: int, seqlens=None) -> np.ndarray:
     """[ceil(q_len/tq), ceil(kv_len/tk)] classes by counting visible elements.
 
     A (q-tile, k-tile) pair is FULL when every in-bounds (query, key) pair of
@@ -330,11 +417,17 @@ def tile_classes_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, j
     positions of the local query share (block `rank`) and of block j.
     Motivation: without skipping, causal ring attention spends about half its
     FLOPs on masked pairs ([TS] "Y nghia thuc te"); devices holding early
-    queries skip most key blocks ([UL] closing remark).
+    queries skip most key blocks ([UL] closing remark). With packed
+    sequences (`seqlens`), q_len == kv_len == sum(seqlens) / N.
     """
-    q_pos = global_positions(layout, n_ring, rank, q_len)
-    k_pos = global_positions(layout, n_ring, j, kv_len)
-    vis = _visibility(q_pos, k_pos, causal)
+    if seqlens is None:
+        q_pos = global_positions(layout, n_ring, rank, q_len)
+        k_pos = global_positions(layout, n_ring, j, kv_len)
+        vis = _visibility(q_pos, k_pos, causal)
+    else:
+        q_seq, q_pos = varlen_positions(layout, n_ring, rank, seqlens)
+        k_seq, k_pos = varlen_positions(layout, n_ring, j, seqlens)
+        vis = _visibility(q_pos, k_pos, causal, q_seq, k_seq)
     nqt = -(-q_len // tq)
     nkt = -(-kv_len // tk)
     out = np.empty((nqt, nkt), dtype=np.int8)
@@ -379,9 +472,17 @@ def tile_class_counts(layout: str, causal: bool, n_ring: int, rank: int, j: int,
     return full, part, skip
 
 
-def visible_pairs_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, block_len: int) -> int:
+def visible_pairs_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, block_len: int,
+                             seqlens=None) -> int:
     """Number of visible (query, key) pairs of one device's share over all
-    blocks, counted element by element."""
+    blocks, counted element by element (packed sequences if `seqlens`)."""
+    if seqlens is not None:
+        q_seq, q_pos = varlen_positions(layout, n_ring, rank, seqlens)
+        total = 0
+        for j in range(n_ring):
+            k_seq, k_pos = varlen_positions(layout, n_ring, j, seqlens)
+            total += int(_visibility(q_pos, k_pos, causal, q_seq, k_seq).sum())
+        return total
     q_pos = global_positions(layout, n_ring, rank, block_len)
     total = 0
     for j in range(n_ring):
@@ -389,18 +490,28 @@ def visible_pairs_bruteforce(layout: str, causal: bool, n_ring: int, rank: int, 
     return total
 
 
-def visible_pairs_closed_form(layout: str, causal: bool, n_ring: int, rank: int, block_len: int) -> int:
+def visible_pairs_closed_form(layout: str, causal: bool, n_ring: int, rank: int, block_len: int,
+                              seqlens=None) -> int:
     """Closed forms (per query head, per batch row):
       non-causal: N B^2
       contiguous causal: r B^2 + B(B+1)/2 (blocks j<r full, j=r triangle, j>r none)
       striped causal: N B(B-1)/2 + (r+1) B (blocks j<=r keep the diagonal,
                       blocks j>r lose it)
+      zigzag causal: (N-1) B^2/2 + B(B+1)/2 for every rank (a block j != r
+                      pairs one chunk before and one after the query chunks:
+                      half of its pairs are visible; j = r is a triangle)
+    Packed sequences: the sum over sequences with B = L_s / N.
     Pinned by: visible_pairs_bruteforce for many (N, B, r)."""
+    if seqlens is not None:
+        return sum(visible_pairs_closed_form(layout, causal, n_ring, rank, int(L) // n_ring)
+                   for L in seqlens)
     n, b, r = n_ring, block_len, rank
     if not causal:
         return n * b * b
     if layout == "contiguous":
         return r * b * b + b * (b + 1) // 2
+    if layout == "zigzag":
+        return (n - 1) * b * b // 2 + b * (b + 1) // 2
     return n * b * (b - 1) // 2 + (r + 1) * b
 
 

@@ -16,12 +16,13 @@ import torch
 
 from oracle import ring_oracle as orc
 from tests.test_oracle_pins import _blocks_from_global, _rand, _sdpa64, _share_rows
+from tests.test_oracle_zigzag_varlen import _masked_sdpa64, _packed_mask, _packed_rows
 
 
 def _pins_hold() -> bool:
     try:
         # GQA, causal and non-causal, both layouts, vs float64 SDPA
-        for layout in ("contiguous", "striped"):
+        for layout in ("contiguous", "striped", "zigzag"):
             for causal in (False, True):
                 n, blen = 3, 4
                 q, k, v = _rand(7, 1, n * blen, 4, 2, 8)
@@ -54,6 +55,33 @@ def _pins_hold() -> bool:
                                 want_c = orc.FULL if all(vis) else (orc.SKIP if not any(vis) else orc.PARTIAL)
                                 if c[qt, kt] != want_c:
                                     return False
+        # positions of all blocks partition the sequence, block by block as placed by hand
+        for layout in ("contiguous", "striped", "zigzag"):
+            for n, blen in ((3, 4), (4, 6)):
+                for j in range(n):
+                    if not np.array_equal(orc.global_positions(layout, n, j, blen),
+                                          _share_rows(layout, n, j, blen)):
+                        return False
+        # packed sequences, every layout, vs SDPA with an explicit block-diagonal mask
+        n, lens = 3, [6, 12, 0, 6]
+        cu = [0, 6, 18, 18, 24]
+        q, k, v = _rand(3, 1, 24, 2, 1, 8)
+        q = 2.0 * q
+        for layout in ("contiguous", "striped", "zigzag"):
+            for causal in (False, True):
+                ref = _masked_sdpa64(q, k, v, _packed_mask(cu, causal))
+                kb = np.stack([k[:, _packed_rows(layout, n, j, cu)] for j in range(n)])
+                vb = np.stack([v[:, _packed_rows(layout, n, j, cu)] for j in range(n)])
+                for r in range(n):
+                    rows = _packed_rows(layout, n, r, cu)
+                    o2, _ = orc.ring_share(q[:, rows], kb, vb, r, n, layout, causal, seqlens=lens)
+                    if not np.allclose(o2, ref[:, rows], atol=1e-10, rtol=0):
+                        return False
+                    seq = np.repeat(np.arange(4), lens)
+                    want = sum(1 for t in rows for u in range(24)
+                               if seq[u] == seq[t] and (u <= t or not causal))
+                    if orc.visible_pairs_closed_form(layout, causal, n, r, 8, seqlens=lens) != want:
+                        return False
         # the page's literal (no max subtraction) form on its worked example size
         q, k, v = _rand(0, 1, 32, 1, 1, 16)
         kb, vb = _blocks_from_global(k, "contiguous", 4), _blocks_from_global(v, "contiguous", 4)
@@ -107,6 +135,33 @@ def _mut_positions_contiguous_off_by_one(layout, n_ring, block, block_len):
     return a * n_ring + block
 
 
+def _mut_zigzag_late_chunk(layout, n_ring, block, block_len):
+    if layout != "zigzag":
+        return _orig_positions(layout, n_ring, block, block_len)
+    a = np.arange(block_len, dtype=np.int64)
+    h = block_len // 2
+    chunk = np.where(a < h, block, 2 * n_ring - block)  # should be 2N-1-block
+    return chunk * h + (a % h)
+
+
+def _mut_zigzag_halves_swapped(layout, n_ring, block, block_len):
+    if layout != "zigzag":
+        return _orig_positions(layout, n_ring, block, block_len)
+    a = np.arange(block_len, dtype=np.int64)
+    h = block_len // 2
+    chunk = np.where(a < h, 2 * n_ring - 1 - block, block)
+    return chunk * h + (a % h)
+
+
+def _mut_varlen_packed_positions(layout, n_ring, block, seqlens):
+    # positions taken over the packed block as if it were one sequence
+    ids, _ = _orig_varlen(layout, n_ring, block, seqlens)
+    total = sum(int(L) for L in seqlens) // n_ring
+    return ids, orc.global_positions(layout, n_ring, block, total)
+
+
+_orig_positions = orc.global_positions
+_orig_varlen = orc.varlen_positions
 _orig_merge = orc.merge_partials
 _orig_block_partial = orc.block_partial
 _orig_visibility = orc._visibility
@@ -135,20 +190,25 @@ def _mut_merge_acc_unscaled(p1, p2):
     return m, l, p1[2] + p2[2]
 
 
-def _mut_visibility_strict(q_pos, k_pos, causal):
+def _mut_visibility_strict(q_pos, k_pos, causal, q_seq=None, k_seq=None):
+    vis = _orig_visibility(q_pos, k_pos, causal, q_seq, k_seq)
+    if causal:
+        vis = vis & (k_pos[None, :] != q_pos[:, None])
+    return vis
+
+
+def _mut_visibility_transposed(q_pos, k_pos, causal, q_seq=None, k_seq=None):
     if not causal:
-        return np.ones((q_pos.size, k_pos.size), dtype=bool)
-    return k_pos[None, :] < q_pos[:, None]
+        return _orig_visibility(q_pos, k_pos, causal, q_seq, k_seq)
+    return _orig_visibility(k_pos, q_pos, causal).T & _orig_visibility(q_pos, k_pos, False, q_seq, k_seq)
 
 
-def _mut_visibility_transposed(q_pos, k_pos, causal):
-    if not causal:
-        return np.ones((q_pos.size, k_pos.size), dtype=bool)
-    return k_pos[None, :] >= q_pos[:, None]
+def _mut_visibility_ignores_sequences(q_pos, k_pos, causal, q_seq=None, k_seq=None):
+    return _orig_visibility(q_pos, k_pos, causal)
 
 
-def _mut_block_partial_transposed_v(q, q_pos, k, v, k_pos, causal, scale=None):
-    m, l, acc = _orig_block_partial(q, q_pos, k, v, k_pos, causal, scale)
+def _mut_block_partial_transposed_v(q, q_pos, k, v, k_pos, causal, scale=None, q_seq=None, k_seq=None):
+    m, l, acc = _orig_block_partial(q, q_pos, k, v, k_pos, causal, scale, q_seq, k_seq)
     return m, l, acc[:, ::-1]
 
 
@@ -161,10 +221,16 @@ def _mut_literal_no_scale(q_share, k_blocks, v_blocks, rank, n_ring, scale=None)
     return _orig_literal(q_share, k_blocks, v_blocks, rank, n_ring, scale=1.0)
 
 
-def _mut_closed_form(layout, causal, n_ring, rank, block_len):
-    if causal and layout == "striped":
+def _mut_closed_form(layout, causal, n_ring, rank, block_len, seqlens=None):
+    if causal and layout == "striped" and seqlens is None:
         return n_ring * block_len * (block_len - 1) // 2 + rank * block_len
-    return _orig_closed(layout, causal, n_ring, rank, block_len)
+    return _orig_closed(layout, causal, n_ring, rank, block_len, seqlens)
+
+
+def _mut_zigzag_closed_form(layout, causal, n_ring, rank, block_len, seqlens=None):
+    if causal and layout == "zigzag" and seqlens is None:
+        return (n_ring - 1) * block_len * block_len // 2 + block_len * (block_len - 1) // 2
+    return _orig_closed(layout, causal, n_ring, rank, block_len, seqlens)
 
 
 def _mut_ring_order(rank, n_ring):
@@ -186,6 +252,11 @@ MUTANTS = {
     "literal_no_scale": ("ring_share_literal", _mut_literal_no_scale),
     "striped_pair_count": ("visible_pairs_closed_form", _mut_closed_form),
     "ring_order_drops_block": ("ring_order", _mut_ring_order),
+    "zigzag_late_chunk_index": ("global_positions", _mut_zigzag_late_chunk),
+    "zigzag_halves_swapped": ("global_positions", _mut_zigzag_halves_swapped),
+    "zigzag_pair_count": ("visible_pairs_closed_form", _mut_zigzag_closed_form),
+    "varlen_crosses_sequences": ("_visibility", _mut_visibility_ignores_sequences),
+    "varlen_packed_positions": ("varlen_positions", _mut_varlen_packed_positions),
 }
 
 

@@ -27,6 +27,22 @@ def _np(t):
     return t.detach().to(torch.float64).cpu().numpy()
 
 
+def _place(t, layout, n_ring, blen):
+    """(block, local index) of global token t, written out per layout
+    (independent of the oracle's position helper)."""
+    if layout == "contiguous":
+        return t // blen, t % blen
+    if layout == "striped":
+        return t % n_ring, t // n_ring
+    # zigzag: 2N chunks of blen/2; chunk c < N is the first half of block c,
+    # chunk c >= N the second half of block 2N-1-c
+    half = blen // 2
+    c = t // half
+    if c < n_ring:
+        return c, t % half
+    return 2 * n_ring - 1 - c, half + t % half
+
+
 def _blocks_from_global(x, layout, n_ring):
     """[B, S, H, d] global -> [N, B, S/N, H, d] by an explicit per-token loop
     (independent of the oracle's position helper)."""
@@ -34,21 +50,18 @@ def _blocks_from_global(x, layout, n_ring):
     blen = seq // n_ring
     out = np.empty((n_ring, bsz, blen, h, d))
     for t in range(seq):
-        if layout == "contiguous":
-            j, a = t // blen, t % blen
-        else:
-            j, a = t % n_ring, t // n_ring
+        j, a = _place(t, layout, n_ring, blen)
         out[j, :, a] = x[:, t]
     return out
 
 
 def _share_rows(layout, n_ring, rank, blen):
     """Global token index of each local query row, by explicit enumeration."""
-    rows = []
+    rows = [None] * blen
     for t in range(n_ring * blen):
-        j = t // blen if layout == "contiguous" else t % n_ring
+        j, a = _place(t, layout, n_ring, blen)
         if j == rank:
-            rows.append(t)
+            rows[a] = t
     return np.array(rows)
 
 
