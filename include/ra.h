@@ -36,7 +36,7 @@
  *     nothing. HIP API failures return RA_ERR_HIP. Work is asynchronous:
  *     device faults surface at the caller's next synchronisation. No C++
  *     exception crosses this ABI.
- *   - Empty problems (batch, q_len or hq*... zero) return RA_OK and enqueue
+ *   - Empty problems (batch or q_len zero) return RA_OK and enqueue
  *     nothing.
  */
 #ifndef RA_H
@@ -59,11 +59,22 @@ typedef enum {
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
-/* Token layouts ([UL] striping remark; contiguous chunks per device).
+/* Token layouts ([UL] striping remark; contiguous chunks per device; [AU]
+ * names zigzag as a variant that rebalances causal work).
  * contiguous: block i holds global tokens [i*B, (i+1)*B).
  * striped:    token t belongs to block t mod N at local index t / N.
+ * zigzag:     the sequence is cut into 2N chunks of B/2 tokens; block i holds
+ *             chunk i (local 0..B/2-1) then chunk 2N-1-i. B must be even.
+ *             Every device then does the same causal work.
  * The caller stores q, k, v already in the layout's token order. */
-typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1 } ra_layout;
+typedef enum {
+  RA_LAYOUT_CONTIGUOUS = 0,
+  RA_LAYOUT_STRIPED = 1,
+  RA_LAYOUT_ZIGZAG = 2
+} ra_layout;
+
+/* Most packed sequences one problem may hold (ra_problem.n_seqs). */
+#define RA_MAX_SEQS 256
 
 /* Class of a (query tile, key tile) pair under the causal mask. */
 typedef enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 } ra_tile_class;
@@ -82,6 +93,20 @@ typedef struct {
   int32_t layout;    /* ra_layout                                            */
   float scale;       /* score scale; <= 0 selects 1/sqrt(head_dim); NaN/inf
                         are invalid                                          */
+  /* Packed variable-length sequences ([TS] "Trade-off thuc te": sequences
+   * of different lengths). n_seqs = 0: one sequence per batch row (the
+   * fields below are ignored). n_seqs >= 1: batch must be 1 and cu_seqlens
+   * is a HOST array of n_seqs + 1 int64 offsets into the packed global
+   * sequence (cu_seqlens[0] = 0, nondecreasing; read during the call only).
+   * Every length L_s = cu_seqlens[s+1] - cu_seqlens[s] must be a multiple of
+   * n_ring (of 2*n_ring for zigzag), and q_len == kv_len ==
+   * cu_seqlens[n_seqs] / n_ring. Each sequence is split over the N blocks by
+   * the layout on its own; a block holds the L_s / N tokens of sequence 0,
+   * then those of sequence 1, and so on. A key is visible to a query only
+   * inside the same sequence (and, if causal, at a position <= the
+   * query's within it). At most RA_MAX_SEQS sequences. */
+  int32_t n_seqs;
+  const int64_t* cu_seqlens;
 } ra_problem;
 
 /*
@@ -96,7 +121,8 @@ typedef struct {
  * For each query row: m = max visible scaled score, l = sum exp(s - m),
  * acc = sum exp(s - m) v. Rows with no visible key get (-inf, 0, 0). Global
  * positions come from (layout, n_ring, rank) for queries and (layout,
- * n_ring, j) for keys; causal masks keys whose position exceeds the query's.
+ * n_ring, j) for keys; causal masks keys whose position exceeds the query's;
+ * packed sequences (n_seqs >= 1) also mask keys of other sequences.
  * Fully masked (query tile, key tile) pairs are never computed.
  * Outputs must not overlap the inputs.
  */
@@ -162,7 +188,8 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
 
 /*
  * Causal tile scheduler, host mirror. Class of the pair (query rows
- * [a_lo, a_hi], keys [b_lo, b_hi]) of block j (local indices, inclusive).
+ * [a_lo, a_hi], keys [b_lo, b_hi]) of block j (local indices, inclusive;
+ * for packed sequences, indices into the packed local share).
  * Returns an ra_tile_class, or -1 on invalid input. The attention kernels
  * decide which tiles to visit and which to mask with the same rule.
  */

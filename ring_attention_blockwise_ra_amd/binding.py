@@ -22,11 +22,13 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libra_amd.so")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(5)
 RA_F32, RA_BF16 = 0, 1
-RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
 RA_TILE_SKIP, RA_TILE_PARTIAL, RA_TILE_FULL = 0, 1, 2
+RA_MAX_SEQS = 256
 
 _LAYOUT = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED,
-           RA_LAYOUT_CONTIGUOUS: RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED: RA_LAYOUT_STRIPED}
+           "zigzag": RA_LAYOUT_ZIGZAG, RA_LAYOUT_CONTIGUOUS: RA_LAYOUT_CONTIGUOUS,
+           RA_LAYOUT_STRIPED: RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG: RA_LAYOUT_ZIGZAG}
 _DTYPE = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 
 EXPORTED = (
@@ -42,7 +44,10 @@ class RaProblem(ctypes.Structure):
         ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int64),
         ("kv_len", ctypes.c_int64), ("n_ring", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("layout", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("n_seqs", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
     ]
+    # keeps the host cu_seqlens array alive as long as the problem
+    _keep = None
 
 
 class RaError(RuntimeError):
@@ -106,13 +111,23 @@ def _stream(s, device) -> ctypes.c_void_p:
 
 
 def make_problem(*, dtype, batch, hq, hkv, head_dim, q_len, kv_len, n_ring, rank, causal,
-                 layout, scale=None) -> RaProblem:
-    return RaProblem(
+                 layout, scale=None, cu_seqlens=None) -> RaProblem:
+    """cu_seqlens: offsets [n_seqs + 1] of packed sequences in the global
+    packed sequence (host list/array/tensor), or None."""
+    p = RaProblem(
         dtype=_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
         batch=int(batch), hq=int(hq), hkv=int(hkv), head_dim=int(head_dim),
         q_len=int(q_len), kv_len=int(kv_len), n_ring=int(n_ring), rank=int(rank),
         causal=int(bool(causal)), layout=_LAYOUT[layout],
         scale=float(scale) if scale is not None else 0.0)
+    if cu_seqlens is not None:
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        p._keep = cu
+        p.n_seqs = max(int(cu.size) - 1, 0)
+        p.cu_seqlens = cu.ctypes.data if cu.size else None
+    return p
 
 
 def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
@@ -130,7 +145,7 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _qkv_problem(q, k, n_ring, rank, causal, layout, scale):
+def _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens=None):
     if q.dim() != 4 or k.dim() < 4:
         raise ValueError("q must be [batch, q_len, hq, d]; k, v [.., batch, kv_len, hkv, d]")
     if q.dtype not in _DTYPE:
@@ -138,14 +153,16 @@ def _qkv_problem(q, k, n_ring, rank, causal, layout, scale):
     b, lq, hq, d = q.shape
     lk, hkv = k.shape[-3], k.shape[-2]
     return make_problem(dtype=q.dtype, batch=b, hq=hq, hkv=hkv, head_dim=d, q_len=lq, kv_len=lk,
-                        n_ring=n_ring, rank=rank, causal=causal, layout=layout, scale=scale)
+                        n_ring=n_ring, rank=rank, causal=causal, layout=layout, scale=scale,
+                        cu_seqlens=cu_seqlens)
 
 
 def ra_block_attn_partial(q, k, v, kv_block_j: int, *, n_ring: int, rank: int, causal: bool,
-                          layout="contiguous", scale=None, m=None, l=None, acc=None, stream=None):
+                          layout="contiguous", scale=None, m=None, l=None, acc=None, stream=None,
+                          cu_seqlens=None):
     """Partial (m, l, acc) of q against KV block kv_block_j (see include/ra.h)."""
     _need(q, "q")
-    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale)
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
     b, lq, hq, d = q.shape
     _need(k, "k", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
     _need(v, "v", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
@@ -208,8 +225,9 @@ def ra_ring_workspace_bytes(prob: RaProblem) -> int:
 
 def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank: int = None,
                 scale=None, out=None, lse=None, want_lse=True, workspace=None,
-                compute_stream=None, copy_stream="auto"):
+                compute_stream=None, copy_stream="auto", cu_seqlens=None):
     """One device's share: q [b, lq, hq, d]; k, v [n_ring, b, lk, hkv, d].
+    cu_seqlens: packed sequences (batch 1), global offsets [n_seqs + 1].
 
     Returns (out fp32 [b, lq, hq, d], lse fp32 [b, lq, hq] or None).
     copy_stream: "auto" (a dedicated side stream per device), None (copies
@@ -218,7 +236,7 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
     if rank is None:
         rank = n_ring - 1
     _need(q, "q")
-    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale)
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
     b, lq, hq, d = q.shape
     dev = q.device
     _need(k, "k", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)

@@ -49,7 +49,41 @@ struct Shape {
   int64_t kv_elems;    // batch * kv_len * hkv * d (one block)
   size_t elem;         // bytes per q/k/v element
   float scale;
+  int32_t packed;      // packed sequences
+  ra::SegTable seg;    // local row segments ({0, q_len} without packing)
 };
+
+static_assert(RA_MAX_SEQS == ra::kMaxSegs, "segment table size");
+
+// Packed sequences: check cu_seqlens and fill the local segment table.
+ra_status validate_packed(const ra_problem* p, Shape* s) {
+  s->packed = p->n_seqs > 0;
+  s->seg.n = 1;
+  s->seg.off[0] = 0;
+  s->seg.off[1] = (int32_t)p->q_len;
+  if (p->n_seqs == 0) return RA_OK;
+  if (p->n_seqs < 0 || p->n_seqs > RA_MAX_SEQS)
+    return fail(RA_ERR_INVALID_ARG, "n_seqs %d out of [0, %d]", p->n_seqs, RA_MAX_SEQS);
+  if (p->cu_seqlens == nullptr) return fail(RA_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (p->batch != 1) return fail(RA_ERR_INVALID_ARG, "packed sequences need batch == 1");
+  if (p->q_len != p->kv_len)
+    return fail(RA_ERR_INVALID_ARG, "packed sequences need q_len == kv_len");
+  if (p->cu_seqlens[0] != 0) return fail(RA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  const int64_t mult = (int64_t)p->n_ring * (p->layout == RA_LAYOUT_ZIGZAG ? 2 : 1);
+  for (int i = 0; i < p->n_seqs; ++i) {
+    const int64_t len = p->cu_seqlens[i + 1] - p->cu_seqlens[i];
+    if (len < 0) return fail(RA_ERR_INVALID_ARG, "cu_seqlens decreases at %d", i + 1);
+    if (len % mult != 0)
+      return fail(RA_ERR_INVALID_ARG, "sequence %d: length %lld is not a multiple of %lld", i,
+                  (long long)len, (long long)mult);
+  }
+  if (p->cu_seqlens[p->n_seqs] != p->q_len * p->n_ring)
+    return fail(RA_ERR_INVALID_ARG, "cu_seqlens[n_seqs] = %lld, expected q_len * n_ring = %lld",
+                (long long)p->cu_seqlens[p->n_seqs], (long long)(p->q_len * p->n_ring));
+  s->seg.n = p->n_seqs;
+  for (int i = 0; i <= p->n_seqs; ++i) s->seg.off[i] = (int32_t)(p->cu_seqlens[i] / p->n_ring);
+  return RA_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -75,8 +109,11 @@ ra_status validate_problem(const ra_problem* p, Shape* s) {
     return fail(RA_ERR_INVALID_ARG, "rank %d out of [0, n_ring=%d)", p->rank, p->n_ring);
   if (p->causal != 0 && p->causal != 1)
     return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", p->causal);
-  if (p->layout != RA_LAYOUT_CONTIGUOUS && p->layout != RA_LAYOUT_STRIPED)
+  if (p->layout != RA_LAYOUT_CONTIGUOUS && p->layout != RA_LAYOUT_STRIPED &&
+      p->layout != RA_LAYOUT_ZIGZAG)
     return fail(RA_ERR_INVALID_ARG, "layout %d unknown", p->layout);
+  if (p->layout == RA_LAYOUT_ZIGZAG && p->n_seqs == 0 && (p->q_len % 2 || p->kv_len % 2))
+    return fail(RA_ERR_INVALID_ARG, "zigzag needs even q_len and kv_len");
   if (p->causal && p->q_len != p->kv_len)
     return fail(RA_ERR_INVALID_ARG, "causal requires q_len == kv_len (%lld vs %lld)",
                 (long long)p->q_len, (long long)p->kv_len);
@@ -88,8 +125,10 @@ ra_status validate_problem(const ra_problem* p, Shape* s) {
   const int64_t group = p->hq / p->hkv;
   if (group * p->q_len > INT32_MAX)
     return fail(RA_ERR_INVALID_ARG, "(hq/hkv)*q_len exceeds 2^31-1");
-  // grid: batch * hkv * ceil(group*q_len/128) workgroups must fit in 2^31
-  const int64_t tiles = (group * p->q_len + 127) / 128;
+  ra_status st = validate_packed(p, s);
+  if (st != RA_OK) return st;
+  // grid: batch * hkv * (row tiles of >= 128 rows per segment) must fit in 2^31
+  const int64_t tiles = (group * p->q_len + 127) / 128 + s->seg.n;
   if ((int64_t)p->batch * p->hkv * tiles > INT32_MAX)
     return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
   s->rows = (int64_t)p->batch * p->q_len * p->hq;
@@ -141,7 +180,8 @@ ra::AttnParams make_params(const ra_problem* p, const Shape& s, int32_t j, const
   a.hkv = p->hkv;
   a.head_dim = p->head_dim;
   a.group = p->hq / p->hkv;
-  a.rows_per_bg = (int32_t)(a.group * p->q_len);
+  a.packed = s.packed;
+  a.seg = s.seg;
   ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
   a.geom_kind = g.kind;
   a.geom_delta = g.delta;
@@ -489,7 +529,8 @@ int32_t ra_tile_class_host(const ra_problem* prob, int32_t kv_block_j, int64_t a
     return -1;
   }
   ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, kv_block_j);
-  return ra::tile_class(g, a_lo, a_hi, b_lo, b_hi);
+  if (s.packed) return ra::tile_class_packed(g, s.seg, a_lo, a_hi, b_lo, b_hi);
+  return ra::tile_class(g, a_lo, a_hi, b_lo, b_hi, prob->kv_len);
 }
 
 static ra_status check_tiles(const ra_problem* prob, int32_t j, int32_t tq, int32_t tk,
@@ -516,7 +557,9 @@ ra_status ra_tile_classes_host(const ra_problem* prob, int32_t kv_block_j, int32
       const int64_t a_lo = qt * tq, a_hi = std::min<int64_t>(a_lo + tq, prob->q_len) - 1;
       for (int64_t kt = 0; kt < nkt; ++kt) {
         const int64_t b_lo = kt * tk, b_hi = std::min<int64_t>(b_lo + tk, prob->kv_len) - 1;
-        out_host[qt * nkt + kt] = (int8_t)ra::tile_class(g, a_lo, a_hi, b_lo, b_hi);
+        out_host[qt * nkt + kt] =
+            (int8_t)(s.packed ? ra::tile_class_packed(g, s.seg, a_lo, a_hi, b_lo, b_hi)
+                              : ra::tile_class(g, a_lo, a_hi, b_lo, b_hi, prob->kv_len));
       }
     }
     return RA_OK;
@@ -536,7 +579,8 @@ ra_status ra_tile_classes_device(const ra_problem* prob, int32_t kv_block_j, int
     if (out_device == nullptr) return fail(RA_ERR_INVALID_ARG, "out is NULL");
     ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, kv_block_j);
     hipError_t e = ra::launch_tile_classes(g.kind, g.delta, prob->q_len, prob->kv_len, tq, tk,
-                                           out_device, static_cast<hipStream_t>(hip_stream));
+                                           s.packed ? &s.seg : nullptr, out_device,
+                                           static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "tile_classes launch");
     return RA_OK;
   } catch (...) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ra_sched.h"
+
 namespace ra {
 
 struct AttnParams {
@@ -23,11 +25,13 @@ struct AttnParams {
   int32_t hkv;
   int32_t head_dim;
   int32_t group;        // hq / hkv
-  int32_t rows_per_bg;  // group * q_len: query rows sharing one KV head
-  int32_t n_row_tiles;  // set by the launcher
+  int32_t packed;       // 1: segment s also owns keys [off[s], off[s+1])
+  int32_t tiles_total;  // set by the launcher: row tiles over all segments
   int32_t geom_kind;    // ra::BlockKind
   int32_t geom_delta;
   float scale_log2;     // scale * log2(e)
+  SegTable seg;         // local row segments (one segment without packing)
+  int32_t tile_off[kMaxSegs + 1];  // set by the launcher: first tile of each segment
 };
 
 // waves: wavefronts per workgroup of the bf16 kernel (4 or 8; 32 rows each).
@@ -40,7 +44,8 @@ hipError_t launch_finalize(int64_t rows, int d, const float* m, const float* l, 
                            float* lse, hipStream_t stream);
 hipError_t launch_fill_empty(int64_t rows, int d, float* m, float* l, float* acc,
                              hipStream_t stream);
+// seg: NULL without packing
 hipError_t launch_tile_classes(int kind, int delta, int64_t q_len, int64_t kv_len, int tq, int tk,
-                               int8_t* out, hipStream_t stream);
+                               const SegTable* seg, int8_t* out, hipStream_t stream);
 
 }  // namespace ra

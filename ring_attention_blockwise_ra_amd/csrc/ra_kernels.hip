@@ -125,6 +125,39 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Work item of one workgroup. The grid is batch x hkv x (row tiles of every
+// segment); within a segment the tiles run last-first, because under the
+// causal rule later rows see more keys (heavy tiles start first).
+struct TileRef {
+  int b, g, tile;  // batch row, KV head, row tile within the segment
+  int row0;        // first local query row of the segment
+  int key0;        // first key of the segment in the block
+  int rows;        // query rows of (segment, KV head): group * segment length
+  int kv_len;      // keys of the segment
+};
+
+__device__ __forceinline__ TileRef locate_tile(const AttnParams& p) {
+  TileRef t;
+  int bid = blockIdx.x;
+  const int per_b = p.hkv * p.tiles_total;
+  t.b = bid / per_b;
+  bid -= t.b * per_b;
+  t.g = bid / p.tiles_total;
+  const int tt = bid - t.g * p.tiles_total;
+  int lo = 0, hi = p.seg.n;  // segment s with tile_off[s] <= tt < tile_off[s+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= tt) lo = mid; else hi = mid;
+  }
+  t.tile = p.tile_off[lo + 1] - 1 - tt;
+  t.row0 = p.seg.off[lo];
+  const int len = p.seg.off[lo + 1] - t.row0;
+  t.rows = len * p.group;
+  t.key0 = p.packed ? t.row0 : 0;
+  t.kv_len = p.packed ? len : p.kv_len;
+  return t;
+}
+
 // Direct global -> LDS copy of one K or V tile (global_load_lds_dwordx4: lane
 // l of an instruction writes bytes [16l, 16l+16) of a 1 KiB LDS segment and
 // reads any global address). Every wave issues LPW instructions, so the
@@ -166,31 +199,26 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // heavy tiles first (causal blocks: larger local index -> more keys)
-  int bid = blockIdx.x;
-  const int per_b = p.hkv * p.n_row_tiles;
-  const int b = bid / per_b;
-  bid -= b * per_b;
-  const int g = bid / p.n_row_tiles;
-  const int tile = p.n_row_tiles - 1 - (bid - g * p.n_row_tiles);
-
-  const int rows_total = p.rows_per_bg;
-  const int rho0 = tile * ROWS;
+  const TileRef tr = locate_tile(p);
+  const int b = tr.b, g = tr.g;
+  const int kv_len = tr.kv_len;
+  const int rows_total = tr.rows;
+  const int rho0 = tr.tile * ROWS;
   const int rho_last = min(rho0 + ROWS, rows_total) - 1;
   const int a_lo = rho0 / p.group;
   const int a_hi = rho_last / p.group;
 
   const BlockGeom geom{p.geom_kind, p.geom_delta};
-  const int key_end = (int)key_end_any(geom, a_hi, p.kv_len);
-  const int full_end = (int)key_end_all(geom, a_lo, p.kv_len);
+  const int key_end = (int)ra::key_end(geom, a_hi, kv_len);
+  const int full_end = (int)ra::key_end(geom, a_lo, kv_len);
   const int n_kt = (key_end + kTK - 1) / kTK;
 
-  const uint16_t* __restrict__ qg = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bstride;
+  const uint16_t* __restrict__ qg = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bstride +
+                                    (int64_t)tr.row0 * p.hq * D;
   const int kv_row_stride = p.hkv * D;
-  const uint16_t* __restrict__ kg =
-      reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.kv_bstride + (int64_t)g * D;
-  const uint16_t* __restrict__ vg =
-      reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.kv_bstride + (int64_t)g * D;
+  const int64_t kv_base = (int64_t)b * p.kv_bstride + (int64_t)tr.key0 * kv_row_stride + (int64_t)g * D;
+  const uint16_t* __restrict__ kg = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
+  const uint16_t* __restrict__ vg = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
 
   // this lane's query row
   const int rho = rho0 + wave * 32 + col;
@@ -199,8 +227,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   const int row_a = rr / p.group;
   const int row_h = g * p.group + (rr - row_a * p.group);
   // last key index visible to this row (keys past kv_len are never visible)
-  const int lim = geom.kind == kAllVisible ? p.kv_len - 1
-                : (geom.kind == kNoneVisible ? -1 : min(row_a - geom.delta, p.kv_len - 1));
+  const int lim = (int)ra::key_end(geom, row_a, kv_len) - 1;
 
   // Q^T fragments (B operand): lane holds dims 16t + 8*half .. +8 of its row
   bf16x8 qf[KSTEPS];
@@ -257,8 +284,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT; };
   auto slot_v = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT + T::TB; };
   auto issue = [&](int t) {
-    dma_tile<D, NW>(kg, kv_row_stride, t * kTK, p.kv_len, slot_k(t), wave, lane);
-    dma_tile<D, NW>(vg, kv_row_stride, t * kTK, p.kv_len, slot_v(t), wave, lane);
+    dma_tile<D, NW>(kg, kv_row_stride, t * kTK, kv_len, slot_k(t), wave, lane);
+    dma_tile<D, NW>(vg, kv_row_stride, t * kTK, kv_len, slot_v(t), wave, lane);
   };
   // Work is done in units of 32 keys: unit u is half u%2 of tile u/2. S(u)
   // is one 32x32 MFMA tile (16 registers per lane), P(u) two bf16x8 operands.
@@ -399,7 +426,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   // ---- epilogue: (m, l, acc) with m in natural units --------------------
   const float lt = sum_xor32(l_run);
   if (row_ok) {
-    const int64_t r = ((int64_t)b * p.q_len + row_a) * p.hq + row_h;
+    const int64_t r = ((int64_t)b * p.q_len + tr.row0 + row_a) * p.hq + row_h;
     if (half == 0) {
       p.m[r] = (m_run == kNegInf) ? kNegInf : m_run * kLn2;
       p.l[r] = lt;
@@ -432,19 +459,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
   __shared__ float sV[kF32TK][D];
 
   const int tid = threadIdx.x;
-  int bid = blockIdx.x;
-  const int per_b = p.hkv * p.n_row_tiles;
-  const int b = bid / per_b;
-  bid -= b * per_b;
-  const int g = bid / p.n_row_tiles;
-  const int tile = p.n_row_tiles - 1 - (bid - g * p.n_row_tiles);
-
-  const int rows_total = p.rows_per_bg;
-  const int rho0 = tile * ROWS;
+  const TileRef tr = locate_tile(p);
+  const int b = tr.b, g = tr.g;
+  const int kv_len = tr.kv_len;
+  const int rows_total = tr.rows;
+  const int rho0 = tr.tile * ROWS;
   const int rho_last = min(rho0 + ROWS, rows_total) - 1;
   const int a_hi = rho_last / p.group;
   const BlockGeom geom{p.geom_kind, p.geom_delta};
-  const int key_end = (int)key_end_any(geom, a_hi, p.kv_len);
+  const int key_end = (int)ra::key_end(geom, a_hi, kv_len);
 
   const int rho = rho0 + tid / TPR;
   const int part = tid % TPR;
@@ -453,12 +476,12 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
   const int a = rr / p.group;
   const int h = g * p.group + (rr - a * p.group);
 
-  const float* __restrict__ qg = reinterpret_cast<const float*>(p.q) + (int64_t)b * p.q_bstride;
-  const float* __restrict__ kgp =
-      reinterpret_cast<const float*>(p.k) + (int64_t)b * p.kv_bstride + (int64_t)g * D;
-  const float* __restrict__ vgp =
-      reinterpret_cast<const float*>(p.v) + (int64_t)b * p.kv_bstride + (int64_t)g * D;
+  const float* __restrict__ qg =
+      reinterpret_cast<const float*>(p.q) + (int64_t)b * p.q_bstride + (int64_t)tr.row0 * p.hq * D;
   const int64_t kv_row_stride = (int64_t)p.hkv * D;
+  const int64_t kv_base = (int64_t)b * p.kv_bstride + (int64_t)tr.key0 * kv_row_stride + (int64_t)g * D;
+  const float* __restrict__ kgp = reinterpret_cast<const float*>(p.k) + kv_base;
+  const float* __restrict__ vgp = reinterpret_cast<const float*>(p.v) + kv_base;
 
   float qv[DC], acc[DC];
   const float* qrow = qg + ((int64_t)a * p.hq + h) * D + part * DC;
@@ -474,8 +497,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
     for (int e = tid; e < kF32TK * D; e += kThreads) {
       int kk = e / D, d = e % D;
       int key = key0 + kk;
-      sK[kk][d] = key < p.kv_len ? kgp[(int64_t)key * kv_row_stride + d] : 0.f;
-      sV[kk][d] = key < p.kv_len ? vgp[(int64_t)key * kv_row_stride + d] : 0.f;
+      sK[kk][d] = key < kv_len ? kgp[(int64_t)key * kv_row_stride + d] : 0.f;
+      sV[kk][d] = key < kv_len ? vgp[(int64_t)key * kv_row_stride + d] : 0.f;
     }
     __syncthreads();
     const int nk = min(kF32TK, key_end - key0);
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
 #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) dot += __shfl_xor(dot, o);
       const int key = key0 + kk;
-      if (visible(geom, a, key)) {
+      if (visible(geom, a, key, kv_len)) {
         const float x = dot * sl2;
         const float m_new = fmaxf(m, x);
         const float alpha = fast_exp2(m - m_new);
@@ -501,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
   }
 
   if (ok) {
-    const int64_t r = ((int64_t)b * p.q_len + a) * p.hq + h;
+    const int64_t r = ((int64_t)b * p.q_len + tr.row0 + a) * p.hq + h;
     if (part == 0) {
       p.m[r] = (m == kNegInf) ? kNegInf : m * kLn2;
       p.l[r] = l;
@@ -587,6 +610,7 @@ __global__ __launch_bounds__(kThreads) void fill_empty_kernel(int64_t rows, int 
 __global__ __launch_bounds__(kThreads) void tile_classes_kernel(int kind, int delta, int64_t q_len,
                                                                  int64_t kv_len, int tq, int tk,
                                                                  int64_t nqt, int64_t nkt,
+                                                                 int packed, SegTable seg,
                                                                  int8_t* out) {
   const int64_t total = nqt * nkt;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -595,7 +619,8 @@ __global__ __launch_bounds__(kThreads) void tile_classes_kernel(int kind, int de
     const int64_t qt = i / nkt, kt = i - qt * nkt;
     const int64_t a_lo = qt * tq, a_hi = min(a_lo + tq, q_len) - 1;
     const int64_t b_lo = kt * tk, b_hi = min(b_lo + tk, kv_len) - 1;
-    out[i] = (int8_t)tile_class(geom, a_lo, a_hi, b_lo, b_hi);
+    out[i] = (int8_t)(packed ? tile_class_packed(geom, seg, a_lo, a_hi, b_lo, b_hi)
+                             : tile_class(geom, a_lo, a_hi, b_lo, b_hi, kv_len));
   }
 }
 
@@ -609,10 +634,23 @@ static int grid_for(int64_t total_threads) {
   return (int)blocks;
 }
 
+// Row tiles of rows_per_tile rows per (segment, KV head); returns the total.
+static int64_t set_tiles(AttnParams& p, int rows_per_tile) {
+  int64_t total = 0;
+  for (int s = 0; s < p.seg.n; ++s) {
+    p.tile_off[s] = (int32_t)total;
+    const int64_t rows = (int64_t)(p.seg.off[s + 1] - p.seg.off[s]) * p.group;
+    total += (rows + rows_per_tile - 1) / rows_per_tile;
+  }
+  p.tile_off[p.seg.n] = (int32_t)total;
+  p.tiles_total = (int32_t)total;
+  return total;
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
   constexpr int ROWS = 32 * NW;
-  p.n_row_tiles = (p.rows_per_bg + ROWS - 1) / ROWS;
+  const int64_t tiles = set_tiles(p, ROWS);
   const size_t smem = kSlots * BfTile<D>::SLOT;  // ring of K/V tile slots
   auto kern = attn_bf16_mfma<D, NW>;
   static bool attr_set = false;  // per instantiation; benign race (idempotent)
@@ -622,7 +660,8 @@ static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t grid = (int64_t)p.batch * p.hkv * p.n_row_tiles;
+  const int64_t grid = (int64_t)p.batch * p.hkv * tiles;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), smem, stream, p);
   return hipGetLastError();
 }
@@ -631,8 +670,8 @@ template <int D>
 static hipError_t launch_f32(AttnParams p, hipStream_t stream) {
   constexpr int DC = D < 32 ? D : 32;
   constexpr int ROWS = kThreads / (D / DC);
-  p.n_row_tiles = (p.rows_per_bg + ROWS - 1) / ROWS;
-  const int64_t grid = (int64_t)p.batch * p.hkv * p.n_row_tiles;
+  const int64_t grid = (int64_t)p.batch * p.hkv * set_tiles(p, ROWS);
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_f32_fma<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -692,10 +731,12 @@ hipError_t launch_fill_empty(int64_t rows, int d, float* m, float* l, float* acc
 }
 
 hipError_t launch_tile_classes(int kind, int delta, int64_t q_len, int64_t kv_len, int tq, int tk,
-                               int8_t* out, hipStream_t stream) {
+                               const SegTable* seg, int8_t* out, hipStream_t stream) {
   const int64_t nqt = (q_len + tq - 1) / tq, nkt = (kv_len + tk - 1) / tk;
+  SegTable t{};
+  if (seg) t = *seg;
   hipLaunchKernelGGL(tile_classes_kernel, dim3(grid_for(nqt * nkt)), dim3(kThreads), 0, stream,
-                     kind, delta, q_len, kv_len, tq, tk, nqt, nkt, out);
+                     kind, delta, q_len, kv_len, tq, tk, nqt, nkt, seg ? 1 : 0, t, out);
   return hipGetLastError();
 }
 

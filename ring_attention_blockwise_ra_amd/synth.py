@@ -46,6 +46,11 @@ CONFIGS = {
     "c5": dict(dtype="bf16", n_ring=8, block=115200, hq=32, hkv=32, d=128, causal=False,
                layouts=("contiguous",), ranks=(0,), seed=5, frame_tokens=256,
                frame_sigma=0.5),
+    # the 1M-token share of c4 with the sequence packed from documents of
+    # mixed lengths (varlen); same token values as c4
+    "c4p": dict(dtype="bf16", n_ring=8, block=131072, hq=32, hkv=8, d=128, causal=True,
+                layouts=("zigzag", "contiguous", "striped"), ranks=(7,), seed=4, k_scale=0.5,
+                values_from="c4", packed=dict(seed=44, min_len=16384, max_len=262144)),
 }
 
 _TENSOR_ID = {"q": 1, "k": 2, "v": 3}
@@ -126,7 +131,7 @@ def config_global(cfg_name: str, device="cpu", q_rows=None):
         if q_rows is not None:
             q = q[:, torch.as_tensor(q_rows, dtype=torch.int64)]
         return q.to(device), k.to(device), v.to(device)
-    c = CONFIGS[cfg_name]
+    c = CONFIGS[CONFIGS[cfg_name].get("values_from", cfg_name)]
     seq = c["n_ring"] * c["block"]
     dt = torch_dtype(c["dtype"])
     extra = {}
@@ -147,3 +152,32 @@ def random_global(seed: int, batch: int, seq: int, hq: int, hkv: int, d: int,
     k = normal_rows("k", seed, batch, seq, hkv, d, device, out_dtype=dt, scale=scale)
     v = normal_rows("v", seed, batch, seq, hkv, d, device, out_dtype=dt, scale=scale)
     return q, k, v
+
+
+def packed_seqlens(total: int, multiple: int, seed: int, min_len: int, max_len: int) -> list[int]:
+    """Lengths of packed sequences filling `total` tokens: log-uniform draws in
+    [min_len, max_len] rounded down to a multiple of `multiple` (at least
+    one multiple), in draw order; the last sequence takes what is left."""
+    g = torch.Generator().manual_seed(seed)
+    lens, used = [], 0
+    lo, hi = torch.log(torch.tensor(float(min_len))), torch.log(torch.tensor(float(max_len)))
+    while True:
+        u = float(torch.rand((), generator=g))
+        L = int(torch.exp(lo + u * (hi - lo))) // multiple * multiple
+        L = max(L, multiple)
+        if used + L >= total:
+            lens.append(total - used)
+            return lens
+        lens.append(L)
+        used += L
+
+
+def config_seqlens(cfg_name: str, layout: str):
+    """Packed sequence lengths of a named workload (None if not packed); each
+    a multiple of 2N so that every layout, zigzag included, can split it."""
+    c = CONFIGS[cfg_name]
+    if "packed" not in c:
+        return None
+    pk = c["packed"]
+    return packed_seqlens(c["n_ring"] * c["block"], 2 * c["n_ring"], pk["seed"], pk["min_len"],
+                          pk["max_len"])

@@ -11,26 +11,35 @@ from __future__ import annotations
 import torch
 
 from . import synth
-from .layout import blocks_from_global, share_tokens
+from .layout import blocks_from_global, packed_blocks_from_global, packed_share_tokens, share_tokens
 
 
-def visible_pairs(layout: str, causal: bool, n_ring: int, rank: int, block_len: int) -> int:
+def visible_pairs(layout: str, causal: bool, n_ring: int, rank: int, block_len: int,
+                  seqlens=None) -> int:
     """Unmasked (query, key) pairs of one share over all N blocks, per head and
     batch row: non-causal N*B^2; contiguous causal r*B^2 + B(B+1)/2 (blocks
     before the share fully visible, its own block a triangle); striped causal
     N*B(B-1)/2 + (r+1)*B (every block a triangle, blocks after the share
-    without their diagonal)."""
+    without their diagonal); zigzag causal (N-1)*B^2/2 + B(B+1)/2 for every
+    rank (half of each other block, a triangle of its own). Packed
+    sequences: the sum over sequences with B = L_s / N."""
+    if seqlens is not None:
+        return sum(visible_pairs(layout, causal, n_ring, rank, int(L) // n_ring) for L in seqlens)
     n, b, r = n_ring, block_len, rank
     if not causal:
         return n * b * b
     if layout == "contiguous":
         return r * b * b + b * (b + 1) // 2
+    if layout == "zigzag":
+        return (n - 1) * b * b // 2 + b * (b + 1) // 2
     return n * b * (b - 1) // 2 + (r + 1) * b
 
 
-def counted_flops(layout, causal, n_ring, rank, block_len, hq, head_dim, batch=1) -> int:
+def counted_flops(layout, causal, n_ring, rank, block_len, hq, head_dim, batch=1,
+                  seqlens=None) -> int:
     """4*d FLOPs (2d for q.k, 2d for p*v) per visible pair per query head."""
-    return 4 * head_dim * hq * batch * visible_pairs(layout, causal, n_ring, rank, block_len)
+    return 4 * head_dim * hq * batch * visible_pairs(layout, causal, n_ring, rank, block_len,
+                                                     seqlens)
 
 
 def prepare(cfg_name: str, layout: str, rank: int, device="cuda", keep_global: bool = False):
@@ -38,15 +47,29 @@ def prepare(cfg_name: str, layout: str, rank: int, device="cuda", keep_global: b
 
     Returns a dict with q [1, B, hq, d], k/v [N, 1, B, hkv, d] (layout order),
     q_tokens (global token index of each local query row), the config dict,
-    and, when keep_global, the global-order k and v.
+    seqlens / cu_seqlens of packed workloads (else None), and, when
+    keep_global, the global-order k and v.
     """
     c = synth.CONFIGS[cfg_name]
     n, blen = c["n_ring"], c["block"]
-    q_tok = share_tokens(layout, n, rank, blen, device="cpu")
+    lens = synth.config_seqlens(cfg_name, layout)
+    cu = None
+    if lens is None:
+        q_tok = share_tokens(layout, n, rank, blen, device="cpu")
+    else:
+        cu = [0]
+        for L in lens:
+            cu.append(cu[-1] + L)
+        q_tok = packed_share_tokens(layout, n, rank, cu, device="cpu")
     q, k_glob, v_glob = synth.config_global(cfg_name, device=device, q_rows=q_tok.to(device))
-    kb = blocks_from_global(k_glob, layout, n)
-    vb = blocks_from_global(v_glob, layout, n)
-    out = dict(cfg=c, q=q.contiguous(), k=kb, v=vb, q_tokens=q_tok, layout=layout, rank=rank)
+    if cu is None:
+        kb = blocks_from_global(k_glob, layout, n)
+        vb = blocks_from_global(v_glob, layout, n)
+    else:
+        kb = packed_blocks_from_global(k_glob, layout, n, cu)
+        vb = packed_blocks_from_global(v_glob, layout, n, cu)
+    out = dict(cfg=c, q=q.contiguous(), k=kb, v=vb, q_tokens=q_tok, layout=layout, rank=rank,
+               seqlens=lens, cu_seqlens=cu)
     if keep_global:
         out["k_global"], out["v_global"] = k_glob, v_glob
     else:

@@ -192,3 +192,79 @@ def test_tile_class_single(L):
     assert B.ra_tile_class_host(prob, 5, 0, 3, 4, 7) == B.RA_TILE_SKIP
     with pytest.raises(B.RaError):
         B.ra_tile_class_host(prob, 5, 0, 16, 0, 3)
+
+
+# ---- zigzag layout and packed sequences -------------------------------------
+def test_tile_classes_host_zigzag_match_bruteforce(L):
+    sizes = [1, 2, 3, 4, 8, 16]
+    for n, blen in [(2, 8), (3, 12), (4, 16), (1, 6), (8, 2)]:
+        for tq, tk in itertools.product(sizes, sizes):
+            for r, j in itertools.product(range(n), range(n)):
+                for causal in (True, False):
+                    prob = _prob(n_ring=n, rank=r, q_len=blen, kv_len=blen, causal=causal,
+                                 layout="zigzag")
+                    got = B.ra_tile_classes_host(prob, j, tq, tk)
+                    want = orc.tile_classes_bruteforce("zigzag", causal, n, r, j, blen, blen, tq, tk)
+                    np.testing.assert_array_equal(np.vectorize(_ORACLE_CLASS.get)(got), want)
+
+
+def test_tile_classes_host_zigzag_real_size_counts(L):
+    blen, t = 131072, 128
+    for r, j in itertools.product([0, 3, 7], range(8)):
+        prob = _prob(n_ring=8, rank=r, q_len=blen, kv_len=blen, layout="zigzag")
+        got = B.ra_tile_classes_host(prob, j, t, t)
+        counts = (int((got == B.RA_TILE_FULL).sum()), int((got == B.RA_TILE_PARTIAL).sum()),
+                  int((got == B.RA_TILE_SKIP).sum()))
+        assert counts == orc.tile_class_counts("zigzag", True, 8, r, j, blen, blen, t, t)
+
+
+PACKED = {
+    "contiguous": [3, 9, 0, 6, 3],
+    "striped": [6, 3, 12, 0],
+    "zigzag": [6, 12, 0, 18, 6],
+}
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_tile_classes_host_packed_match_bruteforce(L, layout):
+    n, lens = 3, PACKED[layout]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    blen = int(cu[-1]) // n
+    for tq, tk in itertools.product([1, 2, 3, 5, 16], [1, 2, 4, 7]):
+        for r, j in itertools.product(range(n), range(n)):
+            for causal in (True, False):
+                prob = _prob(n_ring=n, rank=r, q_len=blen, kv_len=blen, causal=causal,
+                             layout=layout, cu_seqlens=cu)
+                got = B.ra_tile_classes_host(prob, j, tq, tk)
+                want = orc.tile_classes_bruteforce(layout, causal, n, r, j, blen, blen, tq, tk,
+                                                   seqlens=lens)
+                np.testing.assert_array_equal(np.vectorize(_ORACLE_CLASS.get)(got), want)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(layout="zigzag", q_len=255, kv_len=255), b"even"),
+    (dict(cu_seqlens=[0, 512, 1024], batch=2), b"batch == 1"),
+    (dict(cu_seqlens=[0, 512, 1022]), b"multiple"),
+    (dict(cu_seqlens=[0, 600, 512, 1024]), b"decreases"),
+    (dict(cu_seqlens=[4, 512, 1024]), b"cu_seqlens[0]"),
+    (dict(cu_seqlens=[0, 512, 1020]), b"expected q_len * n_ring"),
+    (dict(cu_seqlens=[0, 510, 1024]), b"multiple"),
+    (dict(cu_seqlens=[0, 512, 1032]), b"expected q_len * n_ring"),
+    (dict(cu_seqlens=[0, 4, 1024], layout="zigzag"), b"multiple of 8"),
+    (dict(cu_seqlens=[0, 512, 1024], q_len=256, kv_len=512, causal=0), b"q_len == kv_len"),
+    (dict(cu_seqlens=[0] + [4] * 256 + [1024]), b"n_seqs"),
+])
+def test_packed_and_zigzag_validation(L, kw, msg):
+    prob = _prob(**kw)
+    assert _partial(L, prob) == B.RA_ERR_INVALID_ARG
+    assert msg in L.ra_last_error(), L.ra_last_error()
+    assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) == 0
+
+
+def test_packed_problem_accepted(L):
+    prob = _prob(cu_seqlens=[0, 0, 512, 516, 1024])
+    assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) > 0
+    prob = _prob(cu_seqlens=[0] + [4] * 255 + [1024])  # 256 sequences, all but one empty
+    assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) > 0
+    prob = _prob(layout="zigzag", cu_seqlens=[0, 8, 1024])
+    assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) > 0
