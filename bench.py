@@ -58,7 +58,7 @@ def ring_call(w, out, lse, ws, copy_stream="auto"):
     c = w["cfg"]
     return B.ra_ring_fwd(w["q"], w["k"], w["v"], n_ring=c["n_ring"], causal=c["causal"],
                          layout=w["layout"], rank=w["rank"], out=out, lse=lse, workspace=ws,
-                         copy_stream=copy_stream)
+                         copy_stream=copy_stream, cu_seqlens=w.get("cu_seqlens"))
 
 
 def kernel_leg(w):
@@ -75,20 +75,24 @@ def kernel_leg(w):
     launches = 0
     for s in range(n):
         j = (r - s) % n
-        pairs = block_pairs(w["layout"], c["causal"], n, r, j, blen)
+        pairs = block_pairs(w["layout"], c["causal"], n, r, j, blen, w.get("seqlens"))
         if pairs == 0:
             continue
         ms += timed(lambda: B.ra_block_attn_partial(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
                                                      causal=c["causal"], layout=w["layout"],
-                                                     m=m, l=l, acc=acc))
+                                                     m=m, l=l, acc=acc,
+                                                     cu_seqlens=w.get("cu_seqlens")))
         flops += 4.0 * d * hq * b * pairs
         launches += 1
     return flops, ms, launches
 
 
-def block_pairs(layout, causal, n, r, j, blen):
-    """Visible pairs of one (share, block) per head: full, none, or a
-    triangle with or without its diagonal."""
+def block_pairs(layout, causal, n, r, j, blen, seqlens=None):
+    """Visible pairs of one (share, block) per head: full, none, half (zigzag
+    blocks other than the share's own), or a triangle with or without its
+    diagonal. Packed sequences: the sum over sequences."""
+    if seqlens is not None:
+        return sum(block_pairs(layout, causal, n, r, j, L // n) for L in seqlens)
     if not causal:
         return blen * blen
     if layout == "contiguous":
@@ -97,6 +101,8 @@ def block_pairs(layout, causal, n, r, j, blen):
         if j > r:
             return 0
         return blen * (blen + 1) // 2
+    if layout == "zigzag":
+        return blen * (blen + 1) // 2 if j == r else blen * blen // 2
     return blen * (blen + 1) // 2 if j <= r else blen * (blen - 1) // 2
 
 
@@ -114,13 +120,15 @@ def overlap_leg(w, out, lse, ws, reps=3):
 
     def nocopy():
         B.ra_block_attn_partial(q, w["k"][r], w["v"][r], r, n_ring=n, rank=r, causal=c["causal"],
-                                layout=w["layout"], m=rm, l=rl, acc=out)
+                                layout=w["layout"], m=rm, l=rl, acc=out,
+                                cu_seqlens=w.get("cu_seqlens"))
         for s in range(1, n):
             j = (r - s) % n
-            if block_pairs(w["layout"], c["causal"], n, r, j, c["block"]) == 0:
+            if block_pairs(w["layout"], c["causal"], n, r, j, c["block"], w.get("seqlens")) == 0:
                 continue
             B.ra_block_attn_partial(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
-                                    causal=c["causal"], layout=w["layout"], m=pm, l=pl, acc=pacc)
+                                    causal=c["causal"], layout=w["layout"], m=pm, l=pl, acc=pacc,
+                                    cu_seqlens=w.get("cu_seqlens"))
             B.ra_merge_partials(rm, rl, out, pm, pl, pacc, out=(rm, rl, out))
         B.ra_finalize(rm, rl, out, lse=lse)
 
@@ -194,6 +202,41 @@ def cpu_baseline_leg(w, n_rows, k_global, v_global):
                 seconds=round(dt, 2), host_cpus=len(os.sched_getaffinity(0)))
 
 
+def setup_ring(w, dev):
+    """Outputs, workspace and counted FLOPs of a prepared share."""
+    c = w["cfg"]
+    b, lq, hq, d = w["q"].shape
+    prob = B.make_problem(dtype=w["q"].dtype, batch=b, hq=hq, hkv=w["k"].shape[3], head_dim=d,
+                          q_len=lq, kv_len=w["k"].shape[2], n_ring=c["n_ring"], rank=w["rank"],
+                          causal=c["causal"], layout=w["layout"], cu_seqlens=w.get("cu_seqlens"))
+    w["out"] = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev)
+    w["lse"] = torch.empty(b, lq, hq, dtype=torch.float32, device=dev)
+    w["ws"] = torch.empty(B.ra_ring_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    w["flops"] = workloads.counted_flops(w["layout"], c["causal"], c["n_ring"], w["rank"],
+                                         c["block"], hq, d, b, seqlens=w.get("seqlens"))
+
+
+def widened_leg(dev, cases, reps=2):
+    """Ring TF/s of the same 1M-token share in the layouts and packings
+    beyond the headline pair (one warm-up, median of `reps`)."""
+    res = {}
+    for name, layout in cases:
+        w = workloads.prepare(name, layout, 7, device=dev)
+        setup_ring(w, dev)
+        ring_call(w, w["out"], w["lse"], w["ws"])
+        torch.cuda.synchronize()
+        ts = sorted(timed(lambda: ring_call(w, w["out"], w["lse"], w["ws"])) for _ in range(reps))
+        ms = ts[len(ts) // 2]
+        key = f"{name}_{layout}"
+        res[key] = dict(ms=round(ms, 3), tflops=round(w["flops"] / (ms / 1e3) / 1e12, 2),
+                        counted_flops=w["flops"],
+                        sequences=None if w.get("seqlens") is None else len(w["seqlens"]))
+        del w
+        torch.cuda.empty_cache()
+        log(f"[bench] widened {key} done")
+    return res
+
+
 def load_counters(src_hash):
     """HBM traffic per attention launch from committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
@@ -244,15 +287,7 @@ def main():
         t0 = time.time()
         w = workloads.prepare(args.workload, layout, rank, device=dev,
                               keep_global=(not args.skip_cpu and layout == layouts[0]))
-        b, lq, hq, d = w["q"].shape
-        prob = B.make_problem(dtype=w["q"].dtype, batch=b, hq=hq, hkv=w["k"].shape[3],
-                              head_dim=d, q_len=lq, kv_len=w["k"].shape[2], n_ring=c["n_ring"],
-                              rank=rank, causal=c["causal"], layout=layout)
-        w["out"] = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev)
-        w["lse"] = torch.empty(b, lq, hq, dtype=torch.float32, device=dev)
-        w["ws"] = torch.empty(B.ra_ring_workspace_bytes(prob), dtype=torch.uint8, device=dev)
-        w["flops"] = workloads.counted_flops(layout, c["causal"], c["n_ring"], rank, c["block"],
-                                             hq, d, b)
+        setup_ring(w, dev)
         ws_list.append(w)
         torch.cuda.synchronize()
         log(f"[bench] prepared {layout} in {time.time() - t0:.1f}s")
@@ -372,8 +407,14 @@ def main():
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
         log("[bench] merge leg done")
+        if args.workload == "c4":
+            result["widened"] = dict(
+                note=("same 1M-token causal share, rank 7: zigzag layout, and the sequence "
+                      "packed from mixed-length documents (c4p) in zigzag and contiguous "
+                      "layouts; not part of value"),
+                **widened_leg(dev, [("c4", "zigzag"), ("c4p", "zigzag"), ("c4p", "contiguous")]))
 
-    if not args.skip_cpu:
+    if not args.skip_cpu and ws_list[0].get("cu_seqlens") is None:
         w = ws_list[0]
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows ...")
         result["cpu_baseline"] = cpu_baseline_leg(w, args.cpu_rows, w["k_global"], w["v_global"])
