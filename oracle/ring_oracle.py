@@ -29,7 +29,10 @@ Pages cited (by title and section; the pages are web text on Ring Attention):
        ringuppmarksamhet" (striped and zigzag variants rebalance the work
        that causal masking leaves uneven).
   [TS] also, section "Trade-off thuc te" (practical trade-offs): balancing
-       sequences of different lengths is named as a difficulty.
+       sequences of different lengths is named as a difficulty; and section
+       "Blockwise Backward": the backward pass does not keep the attention
+       matrix but recomputes the attention statistics, each device only on
+       the K/V block visiting it.
 
 Conventions
   * Tensors are [batch, seq, heads, head_dim] (the shape convention of the
@@ -402,6 +405,139 @@ def ring_share_literal(q_share, k_blocks, v_blocks, rank: int, n_ring: int,
                 num[b, :, h, :] += e @ vb[b, :, g, :]
                 den[b, :, h] += e.sum(axis=1)
     return num / den[..., None]
+
+
+# --------------------------------------------------------------------------
+# Backward pass ([TS] "Blockwise Backward").
+#
+# With P = softmax(scale Q K^T) (masked), O = P V and an upstream gradient dO:
+#   dV = P^T dO
+#   dP = dO V^T
+#   dS = P * (dP - D),  D = rowsum(dP * P) = rowsum(dO * O)
+#   dQ = scale dS K,    dK = scale dS^T Q
+# (the derivative of a row softmax: dS_i = P_i (dP_i - P_i . dP_i)). Grouped
+# query heads add their dK, dV into the KV head they read.
+# --------------------------------------------------------------------------
+
+def naive_attention_grad(q, k, v, dout, causal: bool, scale: float | None = None, cu_seqlens=None):
+    """(dq, dk, dv) of O1, the plain definition above, global token order.
+
+    q, dout: [B, S, Hq, d]; k, v: [B, S, Hkv, d]. cu_seqlens: packed
+    sequences (batch 1), attention inside each sequence only.
+    Pinned by: torch autograd through float64 SDPA / an explicit masked
+    softmax, and central finite differences on tiny inputs.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    bsz, seq, hq, d = q.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    pos = np.arange(seq, dtype=np.int64)
+    sid = None
+    if cu_seqlens is not None:
+        sid = np.zeros(seq, dtype=np.int64)
+        cu = [int(c) for c in cu_seqlens]
+        for s in range(len(cu) - 1):
+            sid[cu[s]:cu[s + 1]] = s
+    vis = _visibility(pos, pos, causal, sid, sid)
+    has = vis.any(axis=1)
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(bsz):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            s_ = np.where(vis, (q[b, :, h] @ k[b, :, g].T) * scale, -np.inf)
+            mx = np.where(has, s_.max(axis=1), 0.0)
+            e = np.where(vis, np.exp(s_ - mx[:, None]), 0.0)
+            den = e.sum(axis=1)
+            p = e / np.where(den > 0, den, 1.0)[:, None]
+            o = p @ v[b, :, g]
+            dp = dout[b, :, h] @ v[b, :, g].T
+            delta = (dout[b, :, h] * o).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dq[b, :, h] = scale * ds @ k[b, :, g]
+            dk[b, :, g] += scale * ds.T @ q[b, :, h]
+            dv[b, :, g] += p.T @ dout[b, :, h]
+    return dq, dk, dv
+
+
+def grad_delta(out, dout):
+    """D = rowsum(dO * O) per (batch, row, head): the softmax-derivative term
+    that lets each block's dS be formed without the whole row of P."""
+    return (_f64(out) * _f64(dout)).sum(axis=-1)
+
+
+def block_grad(q, q_pos, k, v, k_pos, dout, lse, delta, causal: bool, scale: float | None = None,
+               q_seq=None, k_seq=None):
+    """One arriving block's share of the backward pass ([TS] "Blockwise
+    Backward": statistics recomputed on the visiting block only):
+        P = exp(scale q k^T - lse) on visible pairs (the saved lse makes it the
+            true softmax restricted to this block's keys, no second pass),
+        dV_j = P^T dO,  dS = P * (dO v^T - D),
+        dQ_j = scale dS k_j,  dK_j = scale dS^T q.
+    Returns (dq_j [B,Lq,Hq,d], dk_j [B,Lk,Hkv,d], dv_j [B,Lk,Hkv,d]).
+    Pinned by: summed over the ring it equals naive_attention_grad."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    lse, delta = _f64(lse), _f64(delta)
+    bsz, lq, hq, d = q.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    vis = _visibility(np.asarray(q_pos, np.int64), np.asarray(k_pos, np.int64), causal,
+                      None if q_seq is None else np.asarray(q_seq, np.int64),
+                      None if k_seq is None else np.asarray(k_seq, np.int64))
+    dq = np.zeros(q.shape)
+    dk, dv = np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(bsz):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            s_ = (q[b, :, h] @ k[b, :, g].T) * scale
+            fin = np.isfinite(lse[b, :, h])
+            base = np.where(fin, lse[b, :, h], 0.0)
+            p = np.where(vis & fin[:, None], np.exp(s_ - base[:, None]), 0.0)
+            dp = dout[b, :, h] @ v[b, :, g].T
+            ds = p * (dp - delta[b, :, h][:, None])
+            dq[b, :, h] = scale * ds @ k[b, :, g]
+            dk[b, :, g] += scale * ds.T @ q[b, :, h]
+            dv[b, :, g] += p.T @ dout[b, :, h]
+    return dq, dk, dv
+
+
+def ring_share_grad(q_share, k_blocks, v_blocks, out, dout, lse, rank: int, n_ring: int,
+                    layout: str, causal: bool, scale: float | None = None, order=None,
+                    seqlens=None):
+    """Backward pass of one device's share over the ring.
+
+    q_share, out, dout: [B, Lq, Hq, d] (out and lse from the forward pass);
+    k_blocks, v_blocks: [N, B, Lk, Hkv, d]. Returns (dq [B,Lq,Hq,d],
+    dk [N,B,Lk,Hkv,d], dv [N,B,Lk,Hkv,d]): dq is complete (queries stay on
+    their device); dk[j], dv[j] are this share's addends to block j's
+    gradients, which in the ring travel with block j and collect every
+    device's addend.
+    Pinned by: the sum over ranks, placed in global order, equals
+    naive_attention_grad; any arrival order gives the same result.
+    """
+    q_share = _f64(q_share)
+    bsz, lq, hq, d = q_share.shape
+    lk = k_blocks.shape[2]
+    if seqlens is None:
+        q_pos, q_seq = global_positions(layout, n_ring, rank, lq), None
+    else:
+        q_seq, q_pos = varlen_positions(layout, n_ring, rank, seqlens)
+    delta = grad_delta(out, dout)
+    dq = np.zeros(q_share.shape)
+    dk = np.zeros(k_blocks.shape)
+    dv = np.zeros(v_blocks.shape)
+    for j in (ring_order(rank, n_ring) if order is None else order):
+        if seqlens is None:
+            k_pos, k_seq = global_positions(layout, n_ring, j, lk), None
+        else:
+            k_seq, k_pos = varlen_positions(layout, n_ring, j, seqlens)
+        gq, gk, gv = block_grad(q_share, q_pos, k_blocks[j], v_blocks[j], k_pos, dout, lse, delta,
+                                causal, scale, q_seq, k_seq)
+        dq += gq
+        dk[j] += gk
+        dv[j] += gv
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------

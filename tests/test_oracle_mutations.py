@@ -266,3 +266,103 @@ def test_pins_catch_mutant(name, monkeypatch):
     monkeypatch.setattr(orc, attr, fn)
     with np.errstate(all="ignore"):
         assert not _pins_hold(), f"mutant {name} survived the pins"
+
+
+# ---------------------------------------------------------------- backward --
+from tests.test_oracle_backward import _torch_grads  # noqa: E402
+
+_orig_block_grad = orc.block_grad
+_orig_naive_grad = orc.naive_attention_grad
+
+
+def _bwd_pins_hold() -> bool:
+    try:
+        n, blen = 3, 4
+        q, k, v = _rand(21, 1, n * blen, 4, 2, 8)
+        q = 2.0 * q
+        dout = np.random.default_rng(4).standard_normal(q.shape)
+        for layout in ("contiguous", "striped", "zigzag"):
+            for causal in (False, True):
+                out, lse = orc.naive_attention(q, k, v, causal)
+                tq, tk, tv, _ = _torch_grads(q, k, v, dout, causal)
+                dq0, dk0, dv0 = orc.naive_attention_grad(q, k, v, dout, causal)
+                if not (np.allclose(dq0, tq, atol=1e-10) and np.allclose(dk0, tk, atol=1e-10)
+                        and np.allclose(dv0, tv, atol=1e-10)):
+                    return False
+                kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+                dk_glob, dv_glob = np.zeros(k.shape), np.zeros(v.shape)
+                for r in range(n):
+                    rows = _share_rows(layout, n, r, blen)
+                    dq, dk, dv = orc.ring_share_grad(q[:, rows], kb, vb, out[:, rows],
+                                                     dout[:, rows], lse[:, rows], r, n, layout,
+                                                     causal)
+                    if not np.allclose(dq, tq[:, rows], atol=1e-10):
+                        return False
+                    for j in range(n):
+                        keys = _share_rows(layout, n, j, blen)
+                        dk_glob[:, keys] += dk[j]
+                        dv_glob[:, keys] += dv[j]
+                if not (np.allclose(dk_glob, tk, atol=1e-10) and np.allclose(dv_glob, tv, atol=1e-10)):
+                    return False
+        return True
+    except (ValueError, IndexError, FloatingPointError):
+        return False
+
+
+def test_unmutated_backward_passes_battery():
+    assert _bwd_pins_hold()
+
+
+def _mut_bg_no_delta(q, q_pos, k, v, k_pos, dout, lse, delta, causal, scale=None, q_seq=None, k_seq=None):
+    return _orig_block_grad(q, q_pos, k, v, k_pos, dout, lse, np.zeros_like(delta), causal, scale,
+                            q_seq, k_seq)
+
+
+def _mut_bg_dk_unscaled(q, q_pos, k, v, k_pos, dout, lse, delta, causal, scale=None, q_seq=None, k_seq=None):
+    dq, dk, dv = _orig_block_grad(q, q_pos, k, v, k_pos, dout, lse, delta, causal, scale, q_seq, k_seq)
+    s = orc.default_scale(q.shape[-1]) if scale is None else scale
+    return dq, dk / s, dv
+
+
+def _mut_bg_local_softmax(q, q_pos, k, v, k_pos, dout, lse, delta, causal, scale=None, q_seq=None, k_seq=None):
+    # renormalises P over the visiting block instead of using the saved lse
+    m, l, _ = orc.block_partial(q, q_pos, k, v, k_pos, causal, scale, q_seq, k_seq)
+    local = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return _orig_block_grad(q, q_pos, k, v, k_pos, dout, local, delta, causal, scale, q_seq, k_seq)
+
+
+def _mut_delta_wrong_operand(out, dout):
+    return (np.asarray(dout, np.float64) ** 2).sum(axis=-1)
+
+
+def _mut_naive_grad_dq_unscaled(q, k, v, dout, causal, scale=None, cu_seqlens=None):
+    dq, dk, dv = _orig_naive_grad(q, k, v, dout, causal, scale, cu_seqlens)
+    s = orc.default_scale(np.asarray(q).shape[-1]) if scale is None else scale
+    return dq / s, dk, dv
+
+
+def _mut_ring_grad_wrong_block(q_share, k_blocks, v_blocks, out, dout, lse, rank, n_ring, layout,
+                               causal, scale=None, order=None, seqlens=None):
+    dq, dk, dv = _orig_ring_grad(q_share, k_blocks, v_blocks, out, dout, lse, rank, n_ring, layout,
+                                 causal, scale, order, seqlens)
+    return dq, np.roll(dk, 1, axis=0), dv
+
+
+_orig_ring_grad = orc.ring_share_grad
+
+BWD_MUTANTS = {
+    "grad_without_delta": ("block_grad", _mut_bg_no_delta),
+    "grad_dk_unscaled": ("block_grad", _mut_bg_dk_unscaled),
+    "grad_block_local_softmax": ("block_grad", _mut_bg_local_softmax),
+    "grad_delta_wrong_operand": ("grad_delta", _mut_delta_wrong_operand),
+    "naive_grad_dq_unscaled": ("naive_attention_grad", _mut_naive_grad_dq_unscaled),
+    "ring_grad_wrong_block": ("ring_share_grad", _mut_ring_grad_wrong_block),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_pins_catch_mutant(name, monkeypatch):
+    attr, fn = BWD_MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    with np.errstate(all="ignore"):
+        assert not _bwd_pins_hold(), f"mutant {name} survived the pins"
