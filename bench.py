@@ -264,6 +264,9 @@ def main():
                     help="before timing, one device copy of this size (counter calibration)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the timed steps (for profiler runs)")
+    ap.add_argument("--skip-aux", action="store_true",
+                    help="no 8192-token overlap and no widened leg, so that every attention "
+                         "launch has the headline workload's shape (kernel-trace runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -390,7 +393,7 @@ def main():
                                  **{k: round(v, 3) for k, v in tot.items()}, per_layout=ov,
                                  note="timing difference below run-to-run spread; see "
                                       "small_workload and the kernel-trace figure")
-        if args.workload != "c2":
+        if args.workload != "c2" and not args.skip_aux:
             w2 = workloads.prepare("c2", "contiguous", 7, device=dev)
             b2, lq2, hq2, d2 = w2["q"].shape
             prob2 = B.make_problem(dtype=w2["q"].dtype, batch=b2, hq=hq2, hkv=w2["k"].shape[3],
@@ -407,7 +410,7 @@ def main():
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
         log("[bench] merge leg done")
-        if args.workload == "c4":
+        if args.workload == "c4" and not args.skip_aux:
             result["widened"] = dict(
                 note=("same 1M-token causal share, rank 7: zigzag layout, and the sequence "
                       "packed from mixed-length documents (c4p) in zigzag and contiguous "
