@@ -460,6 +460,42 @@ def naive_attention_grad(q, k, v, dout, causal: bool, scale: float | None = None
     return dq, dk, dv
 
 
+def naive_grad_rows(q_rows, q_pos, k, v, dout_rows, causal: bool, scale: float | None = None):
+    """dq of selected query rows only (those rows of naive_attention_grad's
+    dq), each from its own visible keys: softmax row P, O = P v,
+    D = dO . O, dS = P (dO v^T - D), dq = scale dS k. For sampled-row checks
+    at sizes where the whole gradient is too large for a CPU.
+
+    q_rows, dout_rows: [B, R, Hq, d] with global positions q_pos [R]; k, v:
+    [B, S, Hkv, d] in global order.
+    Pinned by: equality with naive_attention_grad's dq rows (and autograd)."""
+    q_rows, k, v, dout_rows = _f64(q_rows), _f64(k), _f64(v), _f64(dout_rows)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    bsz, nrows, hq, d = q_rows.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    kmax = int(q_pos.max()) + 1 if causal else k.shape[1]
+    kp = np.arange(kmax, dtype=np.int64)
+    vis = _visibility(q_pos, kp, causal)
+    has = vis.any(axis=1)
+    dq = np.zeros(q_rows.shape)
+    for b in range(bsz):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            kk, vv = k[b, :kmax, g], v[b, :kmax, g]
+            s_ = np.where(vis, (q_rows[b, :, h] @ kk.T) * scale, -np.inf)
+            mx = np.where(has, s_.max(axis=1), 0.0)
+            e = np.where(vis, np.exp(s_ - mx[:, None]), 0.0)
+            den = e.sum(axis=1)
+            p = e / np.where(den > 0, den, 1.0)[:, None]
+            o = p @ vv
+            dp = dout_rows[b, :, h] @ vv.T
+            ds = p * (dp - (dout_rows[b, :, h] * o).sum(axis=1)[:, None])
+            dq[b, :, h] = scale * ds @ kk
+    return dq
+
+
 def grad_delta(out, dout):
     """D = rowsum(dO * O) per (batch, row, head): the softmax-derivative term
     that lets each block's dS be formed without the whole row of P."""

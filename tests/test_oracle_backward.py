@@ -153,3 +153,15 @@ def test_ring_grad_packed():
                 dv_glob[:, keys] += dv[j]
         np.testing.assert_allclose(dk_glob, tk, atol=1e-12, rtol=0)
         np.testing.assert_allclose(dv_glob, tv, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grad_rows_match_whole_gradient(causal):
+    q, k, v = _rand(31, 2, 13, 4, 2, 8)
+    dout = np.random.default_rng(5).standard_normal(q.shape)
+    tq, _, _, _ = _torch_grads(q, k, v, dout, causal)
+    rows = np.array([0, 3, 7, 12])
+    got = orc.naive_grad_rows(q[:, rows], rows, k, v, dout[:, rows], causal)
+    np.testing.assert_allclose(got, tq[:, rows], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(got, orc.naive_attention_grad(q, k, v, dout, causal)[0][:, rows],
+                               atol=1e-13, rtol=0)
