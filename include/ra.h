@@ -204,6 +204,65 @@ ra_status ra_tile_classes_host(const ra_problem* prob, int32_t kv_block_j, int32
 ra_status ra_tile_classes_device(const ra_problem* prob, int32_t kv_block_j, int32_t tq,
                                  int32_t tk, int8_t* out_device, void* hip_stream);
 
+/*
+ * Backward pass ([TS] "Blockwise Backward": the backward does not keep the
+ * attention matrix; it recomputes the attention statistics, each device
+ * only on the K/V block visiting it). With the forward's out and lse and an
+ * upstream gradient dout, for the local queries against block j:
+ *   P  = exp(scale q k^T - lse) on visible pairs,  D = rowsum(dout * out),
+ *   dS = P * (dout v^T - D),
+ *   dq += scale dS k,   dk_j += scale dS^T q,   dv_j += P^T dout
+ * (grouped query heads add into the KV head they read). dq stays with the
+ * queries; dk_j and dv_j are this device's addends to block j's gradients,
+ * which in a ring travel with block j and collect every device's addend.
+ */
+
+/* D = rowsum(dout * out): rows = batch*q_len*hq; out float32 [rows, d];
+ * dout [rows, d] of dtype (RA_BF16 or RA_F32); delta float32 [rows]. */
+ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const float* out,
+                            const void* dout, float* delta, void* hip_stream);
+
+/*
+ * One arriving block's share of the backward pass (addends ACCUMULATED into
+ * dq, dk, dv; the caller zeroes them first when it wants the bare addends).
+ *   q, dout [batch, q_len, hq, head_dim]   dtype
+ *   k, v    [batch, kv_len, hkv, head_dim] dtype: block j
+ *   lse, delta [batch, q_len, hq]          float32 (forward lse; D above)
+ *   dq      [batch, q_len, hq, head_dim]   float32, +=
+ *   dk, dv  [batch, kv_len, hkv, head_dim] float32, +=
+ * Masking, layouts and packed sequences as in ra_block_attn_partial. Rows
+ * whose lse is -inf contribute nothing. dq, dk, dv must not overlap each
+ * other or any input.
+ */
+ra_status ra_block_attn_bwd(const ra_problem* prob, int32_t kv_block_j, const void* q,
+                            const void* k, const void* v, const void* dout, const float* lse,
+                            const float* delta, float* dq, float* dk, float* dv,
+                            void* hip_stream);
+
+/* Workspace bytes ra_ring_bwd needs (0 on invalid input): two staging
+ * buffers for K and two for V, and D. */
+size_t ra_ring_bwd_workspace_bytes(const ra_problem* prob);
+
+/*
+ * One device's whole share of the backward ring, the mirror of ra_ring_fwd:
+ *   q, dout [batch, q_len, hq, head_dim]               dtype
+ *   k, v    [n_ring, batch, kv_len, hkv, head_dim]     dtype (as ra_ring_fwd)
+ *   out     [batch, q_len, hq, head_dim] float32, lse [batch, q_len, hq]
+ *           float32: the forward's results for this share
+ *   dq      [batch, q_len, hq, head_dim] float32: WRITTEN (overwritten)
+ *   dk, dv  [n_ring, batch, kv_len, hkv, head_dim] float32: this share's
+ *           addend to block j is ADDED to dk[j], dv[j] (the accumulators that
+ *           travel with the blocks; calling this for every rank of a ring on
+ *           the same zeroed dk, dv leaves the full key/value gradients)
+ * Step s uses block j = (rank - s) mod N with the forward's staging scheme
+ * (local block in place, the others copied on copy_stream into two staging
+ * buffers, ordered by events). Fully masked blocks are staged, not computed.
+ */
+ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, const void* v,
+                      const float* out, const void* dout, const float* lse, float* dq,
+                      float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream);
+
 /* Thread-local message describing the last failure on this thread. */
 const char* ra_last_error(void);
 

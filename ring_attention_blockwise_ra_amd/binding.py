@@ -34,6 +34,7 @@ _DTYPE = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 EXPORTED = (
     "ra_block_attn_partial", "ra_merge_partials", "ra_finalize", "ra_ring_workspace_bytes",
     "ra_ring_fwd", "ra_tile_class_host", "ra_tile_classes_host", "ra_tile_classes_device",
+    "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
     "ra_last_error",
 )
 
@@ -89,6 +90,14 @@ def lib() -> ctypes.CDLL:
             L.ra_tile_classes_host.restype = I32
             L.ra_tile_classes_device.argtypes = [PP, I32, I32, I32, P, P]
             L.ra_tile_classes_device.restype = I32
+            L.ra_attn_bwd_delta.argtypes = [I64, I32, I32, P, P, P, P]
+            L.ra_attn_bwd_delta.restype = I32
+            L.ra_block_attn_bwd.argtypes = [PP, I32, P, P, P, P, P, P, P, P, P, P]
+            L.ra_block_attn_bwd.restype = I32
+            L.ra_ring_bwd_workspace_bytes.argtypes = [PP]
+            L.ra_ring_bwd_workspace_bytes.restype = ctypes.c_size_t
+            L.ra_ring_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
+            L.ra_ring_bwd.restype = I32
             L.ra_last_error.argtypes = []
             L.ra_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -263,6 +272,98 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
                                  _ptr(lse), _ptr(workspace), workspace.numel(),
                                  ctypes.c_void_p(cs.cuda_stream), xs))
     return out, lse
+
+
+def ra_attn_bwd_delta(out, dout, *, delta=None, stream=None):
+    """delta = rowsum(dout * out) over the last dimension (float32)."""
+    _need(out, "out", torch.float32)
+    _need(dout, "dout", shape=out.shape, device=out.device)
+    if dout.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dout.dtype}")
+    d = out.shape[-1]
+    rows = out.numel() // d if d else 0
+    if delta is None:
+        delta = torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device)
+    _need(delta, "delta", torch.float32, out.shape[:-1], out.device)
+    with torch.cuda.device(out.device):
+        _check(lib().ra_attn_bwd_delta(rows, d, _DTYPE[dout.dtype], _ptr(out), _ptr(dout),
+                                       _ptr(delta), _stream(stream, out.device)))
+    return delta
+
+
+def ra_block_attn_bwd(q, k, v, dout, lse, delta, kv_block_j: int, *, n_ring: int, rank: int,
+                      causal: bool, layout="contiguous", scale=None, dq=None, dk=None, dv=None,
+                      stream=None, cu_seqlens=None):
+    """Block j's backward addends, ACCUMULATED into dq, dk, dv (new zeroed
+    tensors when not given); see include/ra.h."""
+    _need(q, "q")
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
+    b, lq, hq, d = q.shape
+    dev = q.device
+    kshape = (b, prob.kv_len, prob.hkv, d)
+    _need(k, "k", q.dtype, kshape, dev)
+    _need(v, "v", q.dtype, kshape, dev)
+    _need(dout, "dout", q.dtype, q.shape, dev)
+    _need(lse, "lse", torch.float32, (b, lq, hq), dev)
+    _need(delta, "delta", torch.float32, (b, lq, hq), dev)
+    dq = torch.zeros(b, lq, hq, d, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.zeros(kshape, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.zeros(kshape, dtype=torch.float32, device=dev) if dv is None else dv
+    _need(dq, "dq", torch.float32, (b, lq, hq, d), dev)
+    _need(dk, "dk", torch.float32, kshape, dev)
+    _need(dv, "dv", torch.float32, kshape, dev)
+    with torch.cuda.device(dev):
+        _check(lib().ra_block_attn_bwd(ctypes.byref(prob), int(kv_block_j), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _stream(stream, dev)))
+    return dq, dk, dv
+
+
+def ra_ring_bwd_workspace_bytes(prob: RaProblem) -> int:
+    return int(lib().ra_ring_bwd_workspace_bytes(ctypes.byref(prob)))
+
+
+def ra_ring_bwd(q, k, v, out, dout, lse, *, n_ring: int, causal: bool, layout="contiguous",
+                rank: int = None, scale=None, dq=None, dk=None, dv=None, workspace=None,
+                compute_stream=None, copy_stream="auto", cu_seqlens=None):
+    """Backward of one device's share: returns (dq, dk, dv). dq is written;
+    this share's addends are ADDED to dk, dv [n_ring, b, lk, hkv, d] (new
+    zeroed tensors when not given)."""
+    if rank is None:
+        rank = n_ring - 1
+    _need(q, "q")
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
+    b, lq, hq, d = q.shape
+    dev = q.device
+    kshape = (n_ring, b, prob.kv_len, prob.hkv, d)
+    _need(k, "k", q.dtype, kshape, dev)
+    _need(v, "v", q.dtype, kshape, dev)
+    _need(out, "out", torch.float32, (b, lq, hq, d), dev)
+    _need(dout, "dout", q.dtype, q.shape, dev)
+    _need(lse, "lse", torch.float32, (b, lq, hq), dev)
+    dq = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.zeros(kshape, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.zeros(kshape, dtype=torch.float32, device=dev) if dv is None else dv
+    _need(dq, "dq", torch.float32, (b, lq, hq, d), dev)
+    _need(dk, "dk", torch.float32, kshape, dev)
+    _need(dv, "dv", torch.float32, kshape, dev)
+    need = ra_ring_bwd_workspace_bytes(prob)
+    if need == 0 and b * lq * hq > 0:
+        _check(lib().ra_ring_bwd(ctypes.byref(prob), None, None, None, None, None, None, None,
+                                 None, None, None, 0, None, None))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        cs = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
+        if copy_stream == "auto":
+            copy_stream = side_stream(dev)
+        xs = ctypes.c_void_p(None) if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+        _check(lib().ra_ring_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel(),
+                                 ctypes.c_void_p(cs.cuda_stream), xs))
+    return dq, dk, dv
 
 
 _side = {}

@@ -207,7 +207,73 @@ ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const 
   return RA_OK;
 }
 
+ra::BwdParams make_bwd_params(const ra_problem* p, const Shape& s, int32_t j, const void* q,
+                              const void* k, const void* v, const void* dout, const float* lse,
+                              const float* delta, float* dq, float* dk, float* dv) {
+  ra::BwdParams a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.q_bstride = p->q_len * p->hq * p->head_dim;
+  a.kv_bstride = p->kv_len * p->hkv * p->head_dim;
+  a.batch = p->batch;
+  a.q_len = (int32_t)p->q_len;
+  a.kv_len = (int32_t)p->kv_len;
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.head_dim = p->head_dim;
+  a.group = p->hq / p->hkv;
+  a.packed = s.packed;
+  a.seg = s.seg;
+  ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
+  a.geom_kind = g.kind;
+  a.geom_delta = g.delta;
+  a.scale = s.scale;
+  a.scale_log2 = s.scale * 1.4426950408889634f;
+  return a;
+}
+
+// Enqueue one block's backward addends (nothing for a block with no visible
+// pair or no keys: its addends are zero).
+ra_status enqueue_bwd(const ra_problem* p, const Shape& s, int32_t j, const void* q, const void* k,
+                      const void* v, const void* dout, const float* lse, const float* delta,
+                      float* dq, float* dk, float* dv, hipStream_t st) {
+  ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
+  if (g.kind == ra::kNoneVisible || p->kv_len == 0) return RA_OK;
+  ra::BwdParams a = make_bwd_params(p, s, j, q, k, v, dout, lse, delta, dq, dk, dv);
+  hipError_t e = ra::launch_bwd(a, p->dtype == RA_BF16, st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return RA_OK;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct BwdWsLayout {
+  size_t stage_k[2], stage_v[2], delta, total;
+};
+
+BwdWsLayout bwd_ws_layout(const ra_problem* p, const Shape& s) {
+  BwdWsLayout w{};
+  const size_t blk = align256((size_t)s.kv_elems * s.elem);
+  const bool staged = p->n_ring > 1;
+  size_t off = 0;
+  for (int i = 0; i < 2; ++i) {
+    w.stage_k[i] = off;
+    off += staged ? blk : 0;
+    w.stage_v[i] = off;
+    off += staged ? blk : 0;
+  }
+  w.delta = off;
+  off += align256((size_t)s.rows * 4);
+  w.total = off;
+  return w;
+}
 
 struct WsLayout {
   size_t stage_k[2], stage_v[2], pm, pl, pacc, rm, rl, total;
@@ -509,6 +575,194 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
     }
     e = ra::launch_finalize(s.rows, prob->head_dim, rm, rl, out, lse, cs);
     if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const float* out,
+                            const void* dout, float* delta, void* hip_stream) {
+  try {
+    if (rows < 0) return fail(RA_ERR_INVALID_ARG, "rows %lld < 0", (long long)rows);
+    if (dtype != RA_F32 && dtype != RA_BF16)
+      return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_F32 or RA_BF16", dtype);
+    if (head_dim <= 0) return fail(RA_ERR_INVALID_ARG, "head_dim %d <= 0", head_dim);
+    if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+      return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (16, 32, 64, 128)", head_dim);
+    if (rows > (int64_t(1) << 40)) return fail(RA_ERR_INVALID_ARG, "rows too large");
+    const size_t ob = rows * head_dim * 4, db = rows * head_dim * (dtype == RA_BF16 ? 2 : 4);
+    const size_t rb = rows * 4;
+    ra_status st;
+    if ((st = check_ptr(out, ob, "out")) || (st = check_ptr(dout, db, "dout")) ||
+        (st = check_ptr(delta, rb, "delta")))
+      return st;
+    if (overlap(delta, rb, out, ob) || overlap(delta, rb, dout, db))
+      return fail(RA_ERR_INVALID_ARG, "delta must not overlap out or dout");
+    if (rows == 0) return RA_OK;
+    hipError_t e = ra::launch_bwd_delta(rows, head_dim, dtype == RA_BF16, out, dout, delta,
+                                        static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "delta launch");
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+ra_status ra_block_attn_bwd(const ra_problem* prob, int32_t kv_block_j, const void* q,
+                            const void* k, const void* v, const void* dout, const float* lse,
+                            const float* delta, float* dq, float* dk, float* dv,
+                            void* hip_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    if (kv_block_j < 0 || kv_block_j >= prob->n_ring)
+      return fail(RA_ERR_INVALID_ARG, "kv_block_j %d out of [0, n_ring=%d)", kv_block_j,
+                  prob->n_ring);
+    const size_t qb = s.q_elems * s.elem, kb = s.kv_elems * s.elem;
+    const size_t rb = s.rows * 4, qfb = s.q_elems * 4, kfb = s.kv_elems * 4;
+    if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kb, "k")) ||
+        (st = check_ptr(v, kb, "v")) || (st = check_ptr(dout, qb, "dout")) ||
+        (st = check_ptr(lse, rb, "lse")) || (st = check_ptr(delta, rb, "delta")) ||
+        (st = check_ptr(dq, qfb, "dq")) || (st = check_ptr(dk, kfb, "dk")) ||
+        (st = check_ptr(dv, kfb, "dv")))
+      return st;
+    const void* ins[6] = {q, k, v, dout, lse, delta};
+    const size_t insz[6] = {qb, kb, kb, qb, rb, rb};
+    const void* outs[3] = {dq, dk, dv};
+    const size_t outsz[3] = {qfb, kfb, kfb};
+    for (int o = 0; o < 3; ++o) {
+      for (int i = 0; i < 6; ++i)
+        if (overlap(outs[o], outsz[o], ins[i], insz[i]))
+          return fail(RA_ERR_INVALID_ARG, "dq, dk and dv must not overlap any input");
+      for (int o2 = o + 1; o2 < 3; ++o2)
+        if (overlap(outs[o], outsz[o], outs[o2], outsz[o2]))
+          return fail(RA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
+    }
+    if (s.rows == 0) return RA_OK;
+    return enqueue_bwd(prob, s, kv_block_j, q, k, v, dout, lse, delta, dq, dk, dv,
+                       static_cast<hipStream_t>(hip_stream));
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+size_t ra_ring_bwd_workspace_bytes(const ra_problem* prob) {
+  try {
+    Shape s;
+    if (validate_problem(prob, &s) != RA_OK) return 0;
+    return bwd_ws_layout(prob, s).total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, const void* v,
+                      const float* out, const void* dout, const float* lse, float* dq,
+                      float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    const int n = prob->n_ring;
+    const size_t qb = s.q_elems * s.elem, blk = s.kv_elems * s.elem, kvb = blk * n;
+    const size_t qfb = s.q_elems * 4, rb = s.rows * 4, kfb = s.kv_elems * 4 * n;
+    if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kvb, "k")) ||
+        (st = check_ptr(v, kvb, "v")) || (st = check_ptr(out, qfb, "out")) ||
+        (st = check_ptr(dout, qb, "dout")) || (st = check_ptr(lse, rb, "lse")) ||
+        (st = check_ptr(dq, qfb, "dq")) || (st = check_ptr(dk, kfb, "dk")) ||
+        (st = check_ptr(dv, kfb, "dv")))
+      return st;
+    if (blk % 16 != 0 && n > 1)
+      return fail(RA_ERR_INVALID_ARG, "one KV block (%zu bytes) must be a multiple of 16 bytes",
+                  blk);
+    const BwdWsLayout w = bwd_ws_layout(prob, s);
+    if (s.rows > 0) {
+      if (workspace == nullptr || workspace_bytes < w.total)
+        return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+      if (!aligned16(workspace))
+        return fail(RA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    }
+    const void* ins[6] = {q, k, v, out, dout, lse};
+    const size_t insz[6] = {qb, kvb, kvb, qfb, qb, rb};
+    const void* outs[4] = {dq, dk, dv, s.rows > 0 ? workspace : nullptr};
+    const size_t outsz[4] = {qfb, kfb, kfb, w.total};
+    for (int o = 0; o < 4; ++o) {
+      for (int i = 0; i < 6; ++i)
+        if (overlap(outs[o], outsz[o], ins[i], insz[i]))
+          return fail(RA_ERR_INVALID_ARG, "dq, dk, dv and workspace must not overlap any input");
+      for (int o2 = o + 1; o2 < 4; ++o2)
+        if (overlap(outs[o], outsz[o], outs[o2], outsz[o2]))
+          return fail(RA_ERR_INVALID_ARG, "dq, dk, dv and workspace must not overlap each other");
+    }
+    if (s.rows == 0) return RA_OK;
+
+    hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+    hipStream_t xs = static_cast<hipStream_t>(copy_stream);
+    const bool sep = xs != nullptr && xs != cs;
+    DeviceEvents* de = nullptr;
+    if ((st = get_events(&de)) != RA_OK) return st;
+    std::lock_guard<std::mutex> lk(de->mu);
+    if ((st = init_events(de)) != RA_OK) return st;
+
+    char* ws = static_cast<char*>(workspace);
+    const char* kbase = static_cast<const char*>(k);
+    const char* vbase = static_cast<const char*>(v);
+    char* stage_k[2] = {ws + w.stage_k[0], ws + w.stage_k[1]};
+    char* stage_v[2] = {ws + w.stage_v[0], ws + w.stage_v[1]};
+    float* delta = reinterpret_cast<float*>(ws + w.delta);
+    auto block_of = [&](int step) { return ((prob->rank - step) % n + n) % n; };
+    hipError_t e;
+    hipStream_t copy_on = sep ? xs : cs;
+    if (sep) {
+      if ((e = hipEventRecord(de->entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipStreamWaitEvent(xs, de->entry, 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+    }
+    auto stage = [&](int step) -> ra_status {
+      const int j = block_of(step), b = step % 2;
+      hipError_t e2 = hipMemcpyAsync(stage_k[b], kbase + (size_t)j * blk, blk,
+                                     hipMemcpyDeviceToDevice, copy_on);
+      if (e2 == hipSuccess)
+        e2 = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice,
+                            copy_on);
+      if (e2 != hipSuccess) return hip_fail(e2, "staging hipMemcpyAsync");
+      if (sep && (e2 = hipEventRecord(de->copy_done[b], xs)) != hipSuccess)
+        return hip_fail(e2, "hipEventRecord");
+      return RA_OK;
+    };
+    const size_t kelems = (size_t)s.kv_elems;  // floats per block of dk / dv
+
+    // D for every local row, dq from zero, then the ring
+    e = ra::launch_bwd_delta(s.rows, prob->head_dim, prob->dtype == RA_BF16, out, dout, delta, cs);
+    if (e != hipSuccess) return hip_fail(e, "delta launch");
+    e = ra::launch_zero(dq, s.q_elems, cs);
+    if (e != hipSuccess) return hip_fail(e, "zero launch");
+    const int j0 = block_of(0);
+    if ((st = enqueue_bwd(prob, s, j0, q, kbase + (size_t)j0 * blk, vbase + (size_t)j0 * blk,
+                          dout, lse, delta, dq, dk + j0 * kelems, dv + j0 * kelems, cs)) != RA_OK)
+      return st;
+    if (n > 1 && (st = stage(1)) != RA_OK) return st;
+    for (int step = 1; step < n; ++step) {
+      if (step + 1 < n) {
+        if (sep && step - 1 >= 1 &&
+            (e = hipStreamWaitEvent(xs, de->compute_done[(step - 1) % 2], 0)) != hipSuccess)
+          return hip_fail(e, "hipStreamWaitEvent");
+        if ((st = stage(step + 1)) != RA_OK) return st;
+      }
+      const int b = step % 2;
+      if (sep && (e = hipStreamWaitEvent(cs, de->copy_done[b], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      const int j = block_of(step);
+      if ((st = enqueue_bwd(prob, s, j, q, stage_k[b], stage_v[b], dout, lse, delta, dq,
+                            dk + j * kelems, dv + j * kelems, cs)) != RA_OK)
+        return st;
+      if (sep && (e = hipEventRecord(de->compute_done[b], cs)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord");
+    }
     return RA_OK;
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");

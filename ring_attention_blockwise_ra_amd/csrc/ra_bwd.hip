@@ -1,0 +1,846 @@
+// ra_bwd.hip -- gfx950 kernels of the blockwise backward pass.
+//
+// Page (cited by title and section): troisinh.com "Ring Attention -- K/V
+// truyen vong giua GPU, context trieu token", section "Blockwise Backward":
+// the backward pass keeps no attention matrix; it recomputes the attention
+// statistics, each device only on the K/V block visiting it.
+//
+// For the local queries against one block j, with the forward's saved
+// lse (natural log) and D = rowsum(dO * O):
+//   P  = exp(scale q k^T - lse)            (visible pairs; 0 elsewhere)
+//   dP = dO v^T,   dS = P * (dP - D)
+//   dq += scale dS k,   dk += scale dS^T q,   dv += P^T dO
+// dq stays with the queries; dk and dv are this share's addends to block j's
+// gradients (in a ring they travel with the block).
+//
+// Kernels
+//   bwd_delta          D = rowsum(dO * O), one row per D/4 lanes.
+//   bwd_dq_bf16<D,NW>  row tiles of 32*NW query rows (wave: 32 rows), K/V
+//                      tiles of 64 keys streamed through LDS by DMA as in the
+//                      forward kernel. Per 32 keys: S^T = K Q^T and
+//                      dP^T = V dO^T (A from LDS, B = Q^T / dO^T fragments in
+//                      registers), dS^T in registers, dQ^T += K^T dS^T (A =
+//                      K^T by transposed LDS reads, B = dS^T from the
+//                      accumulator layout, as P^T in the forward).
+//   bwd_dkdv_bf16<D,NW> key tiles of 32*NW keys (wave: 32 keys, K and V in
+//                      registers as B operands), query row tiles of 32 rows
+//                      streamed through LDS by DMA. Per row tile:
+//                      S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS),
+//                      dV^T += dO^T P and dK^T += Q^T dS (A by transposed LDS
+//                      reads, B = P / dS straight from the accumulators).
+//   bwd_dq_f32<D>, bwd_dkdv_f32<D>  fp32 inputs, FMA, the same split.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "ra_device.h"
+#include "ra_kernels.h"
+#include "ra_sched.h"
+
+namespace ra {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kPosInf = __builtin_huge_valf();
+
+// lse in natural units -> the exp2-domain subtrahend; a row that saw no key
+// at all (lse = -inf) gets +inf, so its weights are exp2(-inf) = 0.
+__device__ __forceinline__ float lse_to_log2(float lse) {
+  return lse == kNegInf ? kPosInf : lse * kLog2e;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+// A row's vpr = D/4 lanes are consecutive and vpr divides 64, so every row
+// lies inside one wavefront and is reduced with lane exchanges.
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(int64_t rows, int vpr, const f32x4* out,
+                                                              const void* dout, int is_bf16,
+                                                              float* delta) {
+  const int64_t total = rows * vpr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const f32x4 o = out[i];
+    float x0, x1, x2, x3;
+    if (is_bf16) {
+      const u32x2 w = reinterpret_cast<const u32x2*>(dout)[i];
+      x0 = bf16_bits_to_float(w[0] & 0xffffu);
+      x1 = bf16_bits_to_float(w[0] >> 16);
+      x2 = bf16_bits_to_float(w[1] & 0xffffu);
+      x3 = bf16_bits_to_float(w[1] >> 16);
+    } else {
+      const f32x4 w = reinterpret_cast<const f32x4*>(dout)[i];
+      x0 = w[0];
+      x1 = w[1];
+      x2 = w[2];
+      x3 = w[3];
+    }
+    float s = o[0] * x0 + o[1] * x1 + o[2] * x2 + o[3] * x3;
+    for (int off = 1; off < vpr; off <<= 1) s += __shfl_xor(s, off);
+    if ((i % vpr) == 0) delta[i / vpr] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq, bf16 MFMA
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16(BwdParams p) {
+  using T = BfTile<D>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = T::DP / 32;
+  constexpr int LPW = (T::SEGS + NW - 1) / NW;
+  constexpr int LOADS_PER_TILE = 2 * LPW;
+  constexpr int ROWS = 32 * NW;
+
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const TileRef tr = locate_tile(p);
+  const int b = tr.b, g = tr.g;
+  const int kv_len = tr.kv_len;
+  const int rows_total = tr.rows;
+  const int rho0 = tr.tile * ROWS;
+  const int rho_last = min(rho0 + ROWS, rows_total) - 1;
+  const int a_lo = rho0 / p.group;
+  const int a_hi = rho_last / p.group;
+  const BlockGeom geom{p.geom_kind, p.geom_delta};
+  const int key_end = (int)ra::key_end(geom, a_hi, kv_len);
+  const int full_end = (int)ra::key_end(geom, a_lo, kv_len);
+  const int n_kt = (key_end + kTK - 1) / kTK;
+
+  const int64_t q_off = (int64_t)b * p.q_bstride + (int64_t)tr.row0 * p.hq * D;
+  const uint16_t* __restrict__ qg = reinterpret_cast<const uint16_t*>(p.q) + q_off;
+  const uint16_t* __restrict__ og = reinterpret_cast<const uint16_t*>(p.dout) + q_off;
+  const int kv_row_stride = p.hkv * D;
+  const int64_t kv_base = (int64_t)b * p.kv_bstride + (int64_t)tr.key0 * kv_row_stride + (int64_t)g * D;
+  const uint16_t* __restrict__ kg = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
+  const uint16_t* __restrict__ vg = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
+
+  const int rho = rho0 + wave * 32 + col;
+  const bool row_ok = rho < rows_total;
+  const int rr = row_ok ? rho : rows_total - 1;
+  const int row_a = rr / p.group;
+  const int row_h = g * p.group + (rr - row_a * p.group);
+  const int lim = (int)ra::key_end(geom, row_a, kv_len) - 1;
+  const int64_t r = ((int64_t)b * p.q_len + tr.row0 + row_a) * p.hq + row_h;
+  const float lse2 = row_ok ? lse_to_log2(p.lse[r]) : kPosInf;
+  const float dlt = row_ok ? p.delta[r] : 0.f;
+
+  // Q^T and dO^T fragments (B operands): dims 16t + 8*half .. +8 of this row
+  bf16x8 qf[KSTEPS], of[KSTEPS];
+  {
+    const int64_t off = ((int64_t)row_a * p.hq + row_h) * D + 8 * half;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qg + off + 16 * t);
+      u32x4 y = *reinterpret_cast<const u32x4*>(og + off + 16 * t);
+      if (!row_ok) x = y = u32x4{0u, 0u, 0u, 0u};
+      qf[t] = __builtin_bit_cast(bf16x8, x);
+      of[t] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
+  const float sl2 = p.scale_log2;
+
+  // LDS operand offsets, as in the forward kernel: row-major operand reads of
+  // K / V (koff) and transposed reads of K (voff, voff8)
+  int koff[KSTEPS];
+  {
+    const int fr = swz(col) & (T::CPR - 1);
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) koff[t] = col * T::ROWB + (((2 * t + half) ^ fr) & (T::CPR - 1)) * 16;
+  }
+  int voff[DB], voff8[DB];
+  {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int rw = 4 * (grp >> 1) + (sl >> 2);
+    const int lowc = 2 * (grp & 1) + ((sl >> 1) & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = (4 * db + lowc) & (T::CPR - 1);
+      voff[db] = rw * T::ROWB + ((c ^ swz(rw)) & (T::CPR - 1)) * 16 + 8 * (sl & 1);
+      voff8[db] = (rw + 8) * T::ROWB + ((c ^ swz(rw + 8)) & (T::CPR - 1)) * 16 + 8 * (sl & 1);
+    }
+  }
+
+  auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT; };
+  auto slot_v = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT + T::TB; };
+  auto issue = [&](int t) {
+    dma_tile<D, NW>(kg, kv_row_stride, t * kTK, kv_len, slot_k(t), wave, lane);
+    dma_tile<D, NW>(vg, kv_row_stride, t * kTK, kv_len, slot_v(t), wave, lane);
+  };
+  // 32 keys: unit u is half u%2 of tile u/2
+  auto unit = [&](int u) {
+    const char* sK = slot_k(u >> 1) + (u & 1) * 32 * T::ROWB;
+    const char* sV = slot_v(u >> 1) + (u & 1) * 32 * T::ROWB;
+    f32x16 s, dp;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + koff[t]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? f32x16{} : s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + koff[t]);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[t], t == 0 ? f32x16{} : dp, 0, 0, 0);
+    }
+    const int key0 = u * 32;
+    const bool need_mask = key0 + 32 > full_end;
+    const int rel = lim - key0 - 4 * half;
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f32x8 e8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = 8 * c + q;
+        float pv = fast_exp2(__builtin_fmaf(s[i], sl2, -lse2));
+        if (need_mask && 8 * (i >> 2) + (i & 3) > rel) pv = 0.f;
+        e8[q] = pv * (dp[i] - dlt);
+      }
+      dsb[c] = __builtin_convertvector(e8, bf16x8);
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int db = j >> 1, c = j & 1;
+      const s16x4 lo = lds_read_tr16(sK + voff[db] + (c * 16) * T::ROWB);
+      const s16x4 hi = lds_read_tr16(sK + voff8[db] + (c * 16) * T::ROWB);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[c], dqa[db], 0, 0, 0);
+    }
+  };
+
+  if (n_kt > 0) {
+    // Tiles live in a ring of kSlots LDS slots, loads kSlots-1 tiles ahead.
+    // Step t first issues tile t+3 into the slot of tile t-1 (every wave read
+    // it before the barrier that closed step t-1), runs the units of tile t,
+    // then waits until tile t+1 has landed (at most two tiles of its own
+    // loads in flight) and meets the other waves. Tiles past the end are
+    // loaded with clamped rows and never read, so every wave's load count is
+    // uniform.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(0);
+    issue(1);
+    issue(2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    const int n_u = (key_end + 31) / 32;
+    for (int t = 0; t < n_kt; ++t) {
+      issue(t + 3);
+      unit(2 * t);
+      if (2 * t + 1 < n_u) unit(2 * t + 1);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  if (row_ok) {
+    float* drow = p.dq + r * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4) {
+        const int d = db * 32 + 8 * u4 + 4 * half;
+        if (d < D) {
+          f32x4 o = *reinterpret_cast<const f32x4*>(drow + d);
+          o[0] += sc * dqa[db][4 * u4];
+          o[1] += sc * dqa[db][4 * u4 + 1];
+          o[2] += sc * dqa[db][4 * u4 + 2];
+          o[3] += sc * dqa[db][4 * u4 + 3];
+          *reinterpret_cast<f32x4*>(drow + d) = o;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv, bf16 MFMA
+// ---------------------------------------------------------------------------
+// Work item: (batch, KV head, segment, key tile of 32*NW keys); key tiles run
+// first-to-last, because under the causal rule earlier keys are seen by more
+// rows (heavy tiles start first).
+struct KeyTileRef {
+  int b, g, kt;
+  int row0, key0, rows, kv_len, len;
+};
+
+__device__ __forceinline__ KeyTileRef locate_key_tile(const BwdParams& p) {
+  KeyTileRef t;
+  int bid = blockIdx.x;
+  const int per_b = p.hkv * p.tiles_total;
+  t.b = bid / per_b;
+  bid -= t.b * per_b;
+  t.g = bid / p.tiles_total;
+  const int tt = bid - t.g * p.tiles_total;
+  int lo = 0, hi = p.seg.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= tt) lo = mid; else hi = mid;
+  }
+  t.kt = tt - p.tile_off[lo];
+  t.row0 = p.seg.off[lo];
+  t.len = p.seg.off[lo + 1] - t.row0;
+  t.rows = t.len * p.group;
+  t.key0 = p.packed ? t.row0 : 0;
+  t.kv_len = p.packed ? t.len : p.kv_len;
+  return t;
+}
+
+// First local query index whose rows see any key >= k0 (e is nondecreasing).
+__device__ __forceinline__ int first_row_seeing(BlockGeom geom, int k0, int n_rows_a, int kv_len) {
+  int lo = 0, hi = n_rows_a;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (key_end(geom, mid, kv_len) > k0) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+constexpr int kRT = 32;        // query rows per row tile of the dk/dv kernel
+constexpr int kRowSlots = 4;   // LDS ring of row tiles; loads run 3 tiles ahead
+
+template <int D>
+struct RowTile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int TB = kRT * ROWB;          // bytes of one Q (or dO) row tile
+  static constexpr int SEGS = TB / 1024;         // 1 KiB DMA segments
+  static constexpr int ROWS_PER_SEG = 1024 / ROWB;
+  static constexpr int SLOT = 2 * TB;            // Q tile then dO tile
+};
+
+// LDS-DMA of one row tile of q (or dO): rows rho0 .. rho0+31 of (segment, KV
+// head), each gathered from its (query index, head) position; rows past the
+// end are clamped to the last row (loaded, never used: their weights are 0).
+template <int D, int NW>
+__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int hq, int hbase, int group,
+                                         int rho0, int rows_total, char* lds_tile, int wave, int lane) {
+  using R = RowTile<D>;
+  constexpr int LPW = (R::SEGS + NW - 1) / NW;
+  const int rin = lane / R::CPR, pc = lane % R::CPR;
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int seg = (wave + j * NW) % R::SEGS;
+    const int row = seg * R::ROWS_PER_SEG + rin;
+    const int lc = pc ^ (swz(row) & (R::CPR - 1));
+    const int rho = min(rho0 + row, rows_total - 1);
+    const int a = rho / group;
+    const int h = hbase + (rho - a * group);
+    __builtin_amdgcn_global_load_lds((const void*)(src + ((int64_t)a * hq + h) * D + lc * 8),
+                                     (lds_void*)(lds_tile + seg * 1024), 16, 0, 0);
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
+  using T = BfTile<D>;
+  using R = RowTile<D>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = T::DP / 32;
+  constexpr int KEYS = 32 * NW;
+  constexpr int LPW = (R::SEGS + NW - 1) / NW;
+  constexpr int LOADS_PER_TILE = 2 * LPW + 1;  // per wave: Q, dO and the row statistics
+
+  // LDS: ring of (Q tile, dO tile); per wave a ring of row statistics
+  // (lse[32] then delta[32], raw); per wave the key limit of each row
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  float* stats = reinterpret_cast<float*>(smem + kRowSlots * R::SLOT) + wave * kRowSlots * 64;
+  int* elim = reinterpret_cast<int*>(smem + kRowSlots * R::SLOT + NW * kRowSlots * 64 * 4) + wave * 32;
+
+  const KeyTileRef kr = locate_key_tile(p);
+  const int b = kr.b, g = kr.g;
+  const int kv_len = kr.kv_len;
+  const int rows_total = kr.rows;
+  const BlockGeom geom{p.geom_kind, p.geom_delta};
+  const int k0 = kr.kt * KEYS;               // first key of the workgroup (segment-relative)
+  const int kw_lo = k0 + 32 * wave;          // this wave's keys [kw_lo, kw_lo + 32)
+  const int kmy = kw_lo + col;               // this lane's key (B column, output column)
+  const bool key_ok = kmy < kv_len;
+
+  const int kv_row_stride = p.hkv * D;
+  const int64_t kv_base = (int64_t)b * p.kv_bstride + (int64_t)kr.key0 * kv_row_stride + (int64_t)g * D;
+  // K and V fragments as B operands of S = Q K^T and dP = dO V^T: this lane's
+  // key, dims 16t + 8*half .. +8
+  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  {
+    const int kk = min(kmy, kv_len - 1);
+    const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + kv_base + (int64_t)kk * kv_row_stride + 8 * half;
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + kv_base + (int64_t)kk * kv_row_stride + 8 * half;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(kp + 16 * t);
+      u32x4 y = *reinterpret_cast<const u32x4*>(vp + 16 * t);
+      if (!key_ok) x = y = u32x4{0u, 0u, 0u, 0u};
+      kf[t] = __builtin_bit_cast(bf16x8, x);
+      vf[t] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[db][i] = dva[db][i] = 0.f;
+
+  // rows that see any key of the workgroup start at query index a_start
+  const int a_start = first_row_seeing(geom, k0, kr.len, kv_len);
+  const int t_first = (a_start * p.group) / kRT;
+  const int n_rt = (rows_total + kRT - 1) / kRT;
+
+  const int64_t q_off = (int64_t)b * p.q_bstride + (int64_t)kr.row0 * p.hq * D;
+  const uint16_t* __restrict__ qg = reinterpret_cast<const uint16_t*>(p.q) + q_off;
+  const uint16_t* __restrict__ og = reinterpret_cast<const uint16_t*>(p.dout) + q_off;
+  const int64_t st_off = (int64_t)b * p.q_len * p.hq + (int64_t)kr.row0 * p.hq;
+  const int hbase = g * p.group;
+
+  int qoff[KSTEPS];
+  {
+    const int fr = swz(col) & (R::CPR - 1);
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) qoff[t] = col * R::ROWB + (((2 * t + half) ^ fr) & (R::CPR - 1)) * 16;
+  }
+  int voff[DB], voff8[DB];
+  {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int rw = 4 * (grp >> 1) + (sl >> 2);
+    const int lowc = 2 * (grp & 1) + ((sl >> 1) & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = (4 * db + lowc) & (R::CPR - 1);
+      voff[db] = rw * R::ROWB + ((c ^ swz(rw)) & (R::CPR - 1)) * 16 + 8 * (sl & 1);
+      voff8[db] = (rw + 8) * R::ROWB + ((c ^ swz(rw + 8)) & (R::CPR - 1)) * 16 + 8 * (sl & 1);
+    }
+  }
+  const float sl2 = p.scale_log2;
+
+  auto slot_q = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT; };
+  auto slot_o = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT + R::TB; };
+  auto slot_s = [&](int t) { return stats + (t & (kRowSlots - 1)) * 64; };
+  auto issue = [&](int t) {
+    dma_rows<D, NW>(qg, p.hq, hbase, p.group, t * kRT, rows_total, slot_q(t), wave, lane);
+    dma_rows<D, NW>(og, p.hq, hbase, p.group, t * kRT, rows_total, slot_o(t), wave, lane);
+    // lse (lanes 0-31) and delta (lanes 32-63) of rows 32t + col, clamped
+    const int rc = min(t * kRT + col, rows_total - 1);
+    const int a = rc / p.group;
+    const int64_t sidx = st_off + (int64_t)a * p.hq + hbase + (rc - a * p.group);
+    const float* src = half == 0 ? p.lse + sidx : p.delta + sidx;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)slot_s(t), 4, 0, 0);
+  };
+
+  if (t_first < n_rt) {
+    // Ring of kRowSlots row tiles, loads three tiles ahead; step t issues
+    // tile t+3 into the slot of tile t-1 (read before the barrier closing
+    // step t-1) and ends once tile t+1 has landed (two tiles of its own loads
+    // in flight at most). Tiles past the end load clamped rows, never used.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(t_first);
+    issue(t_first + 1);
+    issue(t_first + 2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    for (int t = t_first; t < n_rt; ++t) {
+      issue(t + 3);
+      const int a_lo = (t * kRT) / p.group;
+      const int a_hi = (min(t * kRT + kRT, rows_total) - 1) / p.group;
+      const int e_lo = (int)key_end(geom, a_lo, kv_len);
+      const int e_hi = (int)key_end(geom, a_hi, kv_len);
+      if (kw_lo < e_hi) {  // some key of this wave is visible to some row
+        const bool need_mask = !(kw_lo + 31 < e_lo);
+        if (need_mask && half == 0) {
+          const int rho = t * kRT + col;
+          elim[col] = rho < rows_total ? (int)key_end(geom, rho / p.group, kv_len) : 0;
+        }
+        const char* sQ = slot_q(t);
+        const char* sO = slot_o(t);
+        const float* st = slot_s(t);
+        f32x16 s, dp;
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + qoff[k]);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[k], k == 0 ? f32x16{} : s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sO + qoff[k]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[k], k == 0 ? f32x16{} : dp, 0, 0, 0);
+        }
+        // element i of this lane: row 8*(i/4) + 4*half + i%4 of the tile
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x8 p8, d8;
+#pragma unroll
+          for (int hq4 = 0; hq4 < 2; ++hq4) {
+            const int rbase = 8 * (2 * c + hq4) + 4 * half;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + rbase);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rbase);
+            int e4[4] = {kv_len, kv_len, kv_len, kv_len};
+            if (need_mask) {
+              const u32x4 x = *reinterpret_cast<const u32x4*>(elim + rbase);
+              e4[0] = (int)x[0]; e4[1] = (int)x[1]; e4[2] = (int)x[2]; e4[3] = (int)x[3];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 8 * c + 4 * hq4 + e;
+              const bool rok = t * kRT + rbase + e < rows_total;
+              const float l2 = rok ? lse_to_log2(l4[e]) : kPosInf;
+              float pv = fast_exp2(__builtin_fmaf(s[i], sl2, -l2));
+              if (kmy >= e4[e]) pv = 0.f;
+              p8[4 * hq4 + e] = pv;
+              d8[4 * hq4 + e] = pv * (dp[i] - (rok ? d4[e] : 0.f));
+            }
+          }
+          pb[c] = __builtin_convertvector(p8, bf16x8);
+          dsb[c] = __builtin_convertvector(d8, bf16x8);
+        }
+#pragma unroll
+        for (int j = 0; j < 2 * DB; ++j) {
+          const int db = j >> 1, c = j & 1;
+          const s16x4 olo = lds_read_tr16(sO + voff[db] + (c * 16) * R::ROWB);
+          const s16x4 ohi = lds_read_tr16(sO + voff8[db] + (c * 16) * R::ROWB);
+          const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[c], dva[db], 0, 0, 0);
+          const s16x4 qlo = lds_read_tr16(sQ + voff[db] + (c * 16) * R::ROWB);
+          const s16x4 qhi = lds_read_tr16(sQ + voff8[db] + (c * 16) * R::ROWB);
+          const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[c], dka[db], 0, 0, 0);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  if (key_ok && t_first < n_rt) {
+    const int64_t o = kv_base + (int64_t)kmy * kv_row_stride;
+    float* dkr = p.dk + o;
+    float* dvr = p.dv + o;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4) {
+        const int d = db * 32 + 8 * u4 + 4 * half;
+        if (d < D) {
+          f32x4 x = *reinterpret_cast<const f32x4*>(dkr + d);
+          f32x4 y = *reinterpret_cast<const f32x4*>(dvr + d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] += sc * dka[db][4 * u4 + e];
+            y[e] += dva[db][4 * u4 + e];
+          }
+          *reinterpret_cast<f32x4*>(dkr + d) = x;
+          *reinterpret_cast<f32x4*>(dvr + d) = y;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 FMA backward (exact per-pair arithmetic)
+// ---------------------------------------------------------------------------
+constexpr int kF32Tile = 32;
+
+// dq: thread per (query row, 32-dim slice), keys streamed through LDS
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_f32(BwdParams p) {
+  constexpr int DC = D < 32 ? D : 32;
+  constexpr int TPR = D / DC;
+  constexpr int ROWS = kThreads / TPR;
+  __shared__ float sK[kF32Tile][D];
+  __shared__ float sV[kF32Tile][D];
+  const int tid = threadIdx.x;
+  const TileRef tr = locate_tile(p);
+  const int b = tr.b, g = tr.g, kv_len = tr.kv_len, rows_total = tr.rows;
+  const int rho0 = tr.tile * ROWS;
+  const int a_hi = (min(rho0 + ROWS, rows_total) - 1) / p.group;
+  const BlockGeom geom{p.geom_kind, p.geom_delta};
+  const int key_end = (int)ra::key_end(geom, a_hi, kv_len);
+  const int rho = rho0 + tid / TPR, part = tid % TPR;
+  const bool ok = rho < rows_total;
+  const int rr = ok ? rho : rows_total - 1;
+  const int a = rr / p.group;
+  const int h = g * p.group + (rr - a * p.group);
+  const int64_t r = ((int64_t)b * p.q_len + tr.row0 + a) * p.hq + h;
+  const float lse2 = ok ? lse_to_log2(p.lse[r]) : kPosInf;
+  const float dlt = ok ? p.delta[r] : 0.f;
+  const int64_t kv_row_stride = (int64_t)p.hkv * D;
+  const int64_t kv_base = (int64_t)b * p.kv_bstride + (int64_t)tr.key0 * kv_row_stride + (int64_t)g * D;
+  const float* __restrict__ kgp = reinterpret_cast<const float*>(p.k) + kv_base;
+  const float* __restrict__ vgp = reinterpret_cast<const float*>(p.v) + kv_base;
+  float qv[DC], ov[DC], acc[DC];
+  const float* qrow = reinterpret_cast<const float*>(p.q) + r * D + part * DC;
+  const float* orow = reinterpret_cast<const float*>(p.dout) + r * D + part * DC;
+#pragma unroll
+  for (int i = 0; i < DC; ++i) {
+    qv[i] = ok ? qrow[i] : 0.f;
+    ov[i] = ok ? orow[i] : 0.f;
+    acc[i] = 0.f;
+  }
+  const float sl2 = p.scale_log2;
+  for (int key0 = 0; key0 < key_end; key0 += kF32Tile) {
+    for (int e = tid; e < kF32Tile * D; e += kThreads) {
+      const int kk = e / D, d = e % D, key = key0 + kk;
+      sK[kk][d] = key < kv_len ? kgp[(int64_t)key * kv_row_stride + d] : 0.f;
+      sV[kk][d] = key < kv_len ? vgp[(int64_t)key * kv_row_stride + d] : 0.f;
+    }
+    __syncthreads();
+    const int nk = min(kF32Tile, key_end - key0);
+    for (int kk = 0; kk < nk; ++kk) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < DC; ++i) {
+        s = __builtin_fmaf(qv[i], sK[kk][part * DC + i], s);
+        dp = __builtin_fmaf(ov[i], sV[kk][part * DC + i], dp);
+      }
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        s += __shfl_xor(s, o);
+        dp += __shfl_xor(dp, o);
+      }
+      if (visible(geom, a, key0 + kk, kv_len)) {
+        const float pw = fast_exp2(__builtin_fmaf(s, sl2, -lse2));
+        const float ds = pw * (dp - dlt);
+#pragma unroll
+        for (int i = 0; i < DC; ++i) acc[i] = __builtin_fmaf(ds, sK[kk][part * DC + i], acc[i]);
+      }
+    }
+    __syncthreads();
+  }
+  if (ok) {
+    float* drow = p.dq + r * D + part * DC;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) drow[i] += p.scale * acc[i];
+  }
+}
+
+// dk, dv: thread per (key, 32-dim slice), query rows streamed through LDS
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32(BwdParams p) {
+  constexpr int DC = D < 32 ? D : 32;
+  constexpr int TPR = D / DC;
+  constexpr int KEYS = kThreads / TPR;
+  __shared__ float sQ[kF32Tile][D];
+  __shared__ float sO[kF32Tile][D];
+  __shared__ float sL[kF32Tile], sD[kF32Tile];
+  __shared__ int sE[kF32Tile];
+  const int tid = threadIdx.x;
+  const KeyTileRef kr = locate_key_tile(p);
+  const int b = kr.b, g = kr.g, kv_len = kr.kv_len, rows_total = kr.rows;
+  const BlockGeom geom{p.geom_kind, p.geom_delta};
+  const int k0 = kr.kt * KEYS;
+  const int key = k0 + tid / TPR, part = tid % TPR;
+  const bool key_ok = key < kv_len;
+  const int64_t kv_row_stride = (int64_t)p.hkv * D;
+  const int64_t kv_base = (int64_t)b * p.kv_bstride + (int64_t)kr.key0 * kv_row_stride + (int64_t)g * D;
+  const int kk = min(key, kv_len - 1);
+  const float* krow = reinterpret_cast<const float*>(p.k) + kv_base + (int64_t)kk * kv_row_stride + part * DC;
+  const float* vrow = reinterpret_cast<const float*>(p.v) + kv_base + (int64_t)kk * kv_row_stride + part * DC;
+  float kv_[DC], vv[DC], dk[DC], dv[DC];
+#pragma unroll
+  for (int i = 0; i < DC; ++i) {
+    kv_[i] = key_ok ? krow[i] : 0.f;
+    vv[i] = key_ok ? vrow[i] : 0.f;
+    dk[i] = dv[i] = 0.f;
+  }
+  const int a_start = first_row_seeing(geom, k0, kr.len, kv_len);
+  const int64_t q_off = (int64_t)b * p.q_bstride + (int64_t)kr.row0 * p.hq * D;
+  const float* __restrict__ qg = reinterpret_cast<const float*>(p.q) + q_off;
+  const float* __restrict__ og = reinterpret_cast<const float*>(p.dout) + q_off;
+  const int64_t st_off = (int64_t)b * p.q_len * p.hq + (int64_t)kr.row0 * p.hq;
+  const int hbase = g * p.group;
+  const float sl2 = p.scale_log2;
+  for (int rho0 = (a_start * p.group) / kF32Tile * kF32Tile; rho0 < rows_total; rho0 += kF32Tile) {
+    for (int e = tid; e < kF32Tile * D; e += kThreads) {
+      const int rr = e / D, d = e % D;
+      const int rho = min(rho0 + rr, rows_total - 1);
+      const int a = rho / p.group;
+      const int64_t off = ((int64_t)a * p.hq + hbase + (rho - a * p.group)) * D + d;
+      sQ[rr][d] = qg[off];
+      sO[rr][d] = og[off];
+    }
+    if (tid < kF32Tile) {
+      const int rho = rho0 + tid;
+      const bool rok = rho < rows_total;
+      const int rc = rok ? rho : rows_total - 1;
+      const int a = rc / p.group;
+      const int64_t sidx = st_off + (int64_t)a * p.hq + hbase + (rc - a * p.group);
+      sL[tid] = rok ? lse_to_log2(p.lse[sidx]) : kPosInf;
+      sD[tid] = rok ? p.delta[sidx] : 0.f;
+      sE[tid] = rok ? (int)key_end(geom, a, kv_len) : 0;
+    }
+    __syncthreads();
+    const int nr = min(kF32Tile, rows_total - rho0);
+    for (int rr = 0; rr < nr; ++rr) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < DC; ++i) {
+        s = __builtin_fmaf(sQ[rr][part * DC + i], kv_[i], s);
+        dp = __builtin_fmaf(sO[rr][part * DC + i], vv[i], dp);
+      }
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        s += __shfl_xor(s, o);
+        dp += __shfl_xor(dp, o);
+      }
+      if (key < sE[rr]) {
+        const float pw = fast_exp2(__builtin_fmaf(s, sl2, -sL[rr]));
+        const float ds = pw * (dp - sD[rr]);
+#pragma unroll
+        for (int i = 0; i < DC; ++i) {
+          dv[i] = __builtin_fmaf(pw, sO[rr][part * DC + i], dv[i]);
+          dk[i] = __builtin_fmaf(ds, sQ[rr][part * DC + i], dk[i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (key_ok) {
+    float* dkr = p.dk + kv_base + (int64_t)key * kv_row_stride + part * DC;
+    float* dvr = p.dv + kv_base + (int64_t)key * kv_row_stride + part * DC;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) {
+      dkr[i] += p.scale * dk[i];
+      dvr[i] += dv[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static int64_t set_tiles_bwd(BwdParams& p, int rows_per_tile, bool by_keys) {
+  int64_t total = 0;
+  for (int s = 0; s < p.seg.n; ++s) {
+    p.tile_off[s] = (int32_t)total;
+    const int64_t len = p.seg.off[s + 1] - p.seg.off[s];
+    const int64_t n = by_keys ? (p.packed ? len : (s == 0 ? p.kv_len : 0)) : len * p.group;
+    total += (n + rows_per_tile - 1) / rows_per_tile;
+  }
+  p.tile_off[p.seg.n] = (int32_t)total;
+  p.tiles_total = (int32_t)total;
+  return total;
+}
+
+constexpr int kDqWaves = 8;
+constexpr int kKvWaves = 4;
+
+template <int D>
+static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
+  {
+    BwdParams q = p;
+    const int64_t tiles = set_tiles_bwd(q, 32 * kDqWaves, false);
+    const size_t smem = kSlots * BfTile<D>::SLOT;
+    auto kern = bwd_dq_bf16<D, kDqWaves>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    const int64_t grid = (int64_t)q.batch * q.hkv * tiles;
+    if (grid > 0) hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDqWaves * 64), smem, stream, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    BwdParams q = p;
+    const int64_t tiles = set_tiles_bwd(q, 32 * kKvWaves, true);
+    const size_t smem = kRowSlots * RowTile<D>::SLOT + kKvWaves * (kRowSlots * 64 + 32) * 4;
+    auto kern = bwd_dkdv_bf16<D, kKvWaves>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    const int64_t grid = (int64_t)q.batch * q.hkv * tiles;
+    if (grid > 0) hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kKvWaves * 64), smem, stream, q);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
+  constexpr int DC = D < 32 ? D : 32;
+  constexpr int PER = kThreads / (D / DC);
+  {
+    BwdParams q = p;
+    const int64_t grid = (int64_t)q.batch * q.hkv * set_tiles_bwd(q, PER, false);
+    if (grid > 0) hipLaunchKernelGGL(bwd_dq_f32<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    BwdParams q = p;
+    const int64_t grid = (int64_t)q.batch * q.hkv * set_tiles_bwd(q, PER, true);
+    if (grid > 0) hipLaunchKernelGGL(bwd_dkdv_f32<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t stream) {
+  if (is_bf16) {
+    switch (p.head_dim) {
+      case 16: return launch_bwd_bf16<16>(p, stream);
+      case 32: return launch_bwd_bf16<32>(p, stream);
+      case 64: return launch_bwd_bf16<64>(p, stream);
+      case 128: return launch_bwd_bf16<128>(p, stream);
+    }
+  } else {
+    switch (p.head_dim) {
+      case 16: return launch_bwd_f32<16>(p, stream);
+      case 32: return launch_bwd_f32<32>(p, stream);
+      case 64: return launch_bwd_f32<64>(p, stream);
+      case 128: return launch_bwd_f32<128>(p, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(int64_t n4, f32x4* x) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+hipError_t launch_zero(float* x, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;  // callers pass multiples of 4 (rows * head_dim)
+  int64_t blocks = (n4 + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, n4,
+                     reinterpret_cast<f32x4*>(x));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(int64_t rows, int d, int is_bf16, const float* out, const void* dout,
+                            float* delta, hipStream_t stream) {
+  const int vpr = d / 4;
+  int64_t blocks = (rows * vpr + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, rows, vpr,
+                     reinterpret_cast<const f32x4*>(out), dout, is_bf16, delta);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -34,6 +34,44 @@ struct AttnParams {
   int32_t tile_off[kMaxSegs + 1];  // set by the launcher: first tile of each segment
 };
 
+// Backward pass of one block: dq += its dQ addend, dk/dv += its dK/dV addends.
+struct BwdParams {
+  const void* q;        // [batch, q_len, hq, D]
+  const void* k;        // [batch, kv_len, hkv, D] (one block)
+  const void* v;
+  const void* dout;     // [batch, q_len, hq, D], same dtype as q
+  const float* lse;     // [batch, q_len, hq], natural log
+  const float* delta;   // [batch, q_len, hq]: rowsum(dout * out)
+  float* dq;            // [batch, q_len, hq, D], accumulated
+  float* dk;            // [batch, kv_len, hkv, D], accumulated
+  float* dv;
+  int64_t q_bstride;
+  int64_t kv_bstride;
+  int32_t batch;
+  int32_t q_len;
+  int32_t kv_len;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t group;
+  int32_t packed;
+  int32_t tiles_total;  // set by the launcher (row tiles or key tiles)
+  int32_t geom_kind;
+  int32_t geom_delta;
+  float scale;          // natural units
+  float scale_log2;     // scale * log2(e)
+  SegTable seg;
+  int32_t tile_off[kMaxSegs + 1];
+};
+
+// dq kernel then dk/dv kernel of one block, on one stream.
+hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t stream);
+// x[0 .. n) = 0 (n a multiple of 4), a kernel rather than a memset.
+hipError_t launch_zero(float* x, int64_t n, hipStream_t stream);
+// delta[r] = sum_d dout[r, d] * out[r, d]; dout in the input dtype.
+hipError_t launch_bwd_delta(int64_t rows, int d, int is_bf16, const float* out, const void* dout,
+                            float* delta, hipStream_t stream);
+
 // waves: wavefronts per workgroup of the bf16 kernel (4 or 8; 32 rows each).
 hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream);
 

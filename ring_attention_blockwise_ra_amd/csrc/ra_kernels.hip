@@ -27,26 +27,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "ra_device.h"
 #include "ra_kernels.h"
 #include "ra_sched.h"
 
 namespace ra {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegInf = -__builtin_huge_valf();
-// the exponent reference moves only when the running max passes it by more
-// than this (log2 units): weights stay <= 2^kRescale
-constexpr float kRescale = 8.0f;
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention partial
@@ -78,107 +63,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 16-bit element of the 8 bytes addressed by source lane 4j + i/4. Source lane
 // s therefore addresses V[k0 + s/4][d0 + 4(s%4)], and output lane i receives
 // V[k0 .. k0+3][d0 + i]: four consecutive keys of one head dimension.
-
-constexpr int kThreads = 256;  // workgroup size of the fp32 and elementwise kernels
-constexpr int kTK = 64;        // keys per tile
-constexpr int kSlots = 4;      // LDS ring of K/V tiles; loads run kSlots-1 tiles ahead
-
-// LDS layout of one K or V tile: 64 rows (keys) of D bf16, no padding. Each
-// 16-byte chunk c of row r is stored at chunk position c ^ f(r) with
-// f(r) = 4*(r%4) + (r/4)%4 (masked to the chunks of a row). The LDS has 64
-// banks of 4 bytes, so a 256-byte row spans every bank once and a chunk's
-// banks depend only on its position in the row. f is a bijection on any 16
-// consecutive rows, so the 16-byte K operand reads (16 rows, one chunk, per
-// bank cycle) are conflict-free; and f/4 differs across the 4 rows of a
-// transposed V read, so its 4 rows x 4 adjacent chunks are too (measured:
-// 200 and 148 bytes/clock per CU for the two patterns, against 120 and 115
-// for a swizzle that only varies over 8 rows).
-template <int D>
-struct BfTile {
-  static constexpr int DP = D < 32 ? 32 : D;       // head dims padded to the MFMA M of 32
-  static constexpr int ROWB = D * 2;               // bytes per key row
-  static constexpr int CPR = D / 8;                // 16-byte chunks per row
-  static constexpr int TB = kTK * ROWB;            // bytes per K (or V) tile
-  static constexpr int SLOT = 2 * TB;              // K tile then V tile
-  static constexpr int SEGS = TB / 1024;           // 1 KiB DMA segments per tile
-  static constexpr int ROWS_PER_SEG = 1024 / ROWB;
-};
-
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-__device__ __forceinline__ float max_xor32(float x) {
-  // max with the value held by lane L^32 (one lane swap across the wave halves)
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-
-__device__ __forceinline__ float sum_xor32(float x) {
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-}
-
-// Work item of one workgroup. The grid is batch x hkv x (row tiles of every
-// segment); within a segment the tiles run last-first, because under the
-// causal rule later rows see more keys (heavy tiles start first).
-struct TileRef {
-  int b, g, tile;  // batch row, KV head, row tile within the segment
-  int row0;        // first local query row of the segment
-  int key0;        // first key of the segment in the block
-  int rows;        // query rows of (segment, KV head): group * segment length
-  int kv_len;      // keys of the segment
-};
-
-__device__ __forceinline__ TileRef locate_tile(const AttnParams& p) {
-  TileRef t;
-  int bid = blockIdx.x;
-  const int per_b = p.hkv * p.tiles_total;
-  t.b = bid / per_b;
-  bid -= t.b * per_b;
-  t.g = bid / p.tiles_total;
-  const int tt = bid - t.g * p.tiles_total;
-  int lo = 0, hi = p.seg.n;  // segment s with tile_off[s] <= tt < tile_off[s+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tile_off[mid] <= tt) lo = mid; else hi = mid;
-  }
-  t.tile = p.tile_off[lo + 1] - 1 - tt;
-  t.row0 = p.seg.off[lo];
-  const int len = p.seg.off[lo + 1] - t.row0;
-  t.rows = len * p.group;
-  t.key0 = p.packed ? t.row0 : 0;
-  t.kv_len = p.packed ? len : p.kv_len;
-  return t;
-}
-
-// Direct global -> LDS copy of one K or V tile (global_load_lds_dwordx4: lane
-// l of an instruction writes bytes [16l, 16l+16) of a 1 KiB LDS segment and
-// reads any global address). Every wave issues LPW instructions, so the
-// per-wave count of outstanding loads is the same in all waves. Key rows past
-// kv_len re-read the last row; those keys are masked before the softmax.
-template <int D, int NW>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int row_stride, int key0,
-                                         int kv_len, char* lds_tile, int wave, int lane) {
-  using T = BfTile<D>;
-  constexpr int LPW = T::SEGS >= NW ? T::SEGS / NW : 1;
-  const int rin = lane / T::CPR, pc = lane % T::CPR;
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int seg = (wave + j * NW) % T::SEGS;
-    const int row = seg * T::ROWS_PER_SEG + rin;
-    const int lc = pc ^ (swz(row) & (T::CPR - 1));
-    const int key = min(key0 + row, kv_len - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + key * row_stride + lc * 8),
-                                     (lds_void*)(lds_tile + seg * 1024), 16, 0, 0);
-  }
-}
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {

@@ -268,3 +268,45 @@ def test_packed_problem_accepted(L):
     assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) > 0
     prob = _prob(layout="zigzag", cu_seqlens=[0, 8, 1024])
     assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) > 0
+
+
+# ---- backward entry points ---------------------------------------------------
+def test_backward_validation_before_any_hip_call(L):
+    bad = _prob(head_dim=96)
+    args = [FAKE] * 9
+    assert L.ra_block_attn_bwd(ctypes.byref(bad), 0, *args, None) == B.RA_ERR_UNSUPPORTED
+    assert L.ra_ring_bwd_workspace_bytes(ctypes.byref(bad)) == 0
+    prob = _prob()
+    assert L.ra_block_attn_bwd(ctypes.byref(prob), 9, *args, None) == B.RA_ERR_INVALID_ARG
+    assert b"kv_block_j" in L.ra_last_error()
+    a = [FAKE] * 9
+    a[3] = None  # dout
+    assert L.ra_block_attn_bwd(ctypes.byref(prob), 0, *a, None) == B.RA_ERR_INVALID_ARG
+    assert b"dout is NULL" in L.ra_last_error()
+    # dq aliasing q is refused
+    assert L.ra_block_attn_bwd(ctypes.byref(prob), 0, *args, None) == B.RA_ERR_INVALID_ARG
+    assert b"overlap" in L.ra_last_error()
+    assert L.ra_attn_bwd_delta(10, 64, 5, FAKE, FAKE, FAKE, None) == B.RA_ERR_INVALID_ARG
+    assert L.ra_attn_bwd_delta(10, 48, B.RA_BF16, FAKE, FAKE, FAKE, None) == B.RA_ERR_UNSUPPORTED
+    assert L.ra_attn_bwd_delta(0, 64, B.RA_BF16, None, None, None, None) == B.RA_OK
+
+
+def test_ring_bwd_workspace_and_checks(L):
+    prob = _prob(n_ring=4, q_len=256, kv_len=256)
+    need = L.ra_ring_bwd_workspace_bytes(ctypes.byref(prob))
+    blk = 1 * 256 * 2 * 64 * 2
+    rows = 1 * 256 * 4
+    assert need >= 4 * blk + rows * 4
+    base = 0x100000
+    ptr = lambda off: ctypes.c_void_p(base + off)  # noqa: E731
+    big = 1 << 24
+    args = [ptr(i * big) for i in range(9)]  # q k v out dout lse dq dk dv
+    assert L.ra_ring_bwd(ctypes.byref(prob), *args, None, 0, None, None) == B.RA_ERR_WORKSPACE
+    assert L.ra_ring_bwd(ctypes.byref(prob), *args, ptr(11 * big), need - 1, None, None) \
+        == B.RA_ERR_WORKSPACE
+    assert b"workspace of" in L.ra_last_error()
+    # workspace overlapping dq
+    assert L.ra_ring_bwd(ctypes.byref(prob), *args, ptr(6 * big), need, None, None) \
+        == B.RA_ERR_INVALID_ARG
+    one = _prob(n_ring=1, rank=0)
+    assert L.ra_ring_bwd_workspace_bytes(ctypes.byref(one)) < need  # no staging buffers
