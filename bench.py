@@ -237,6 +237,53 @@ def widened_leg(dev, cases, reps=2):
     return res
 
 
+def backward_leg(dev, layouts, reps=1):
+    """Backward ring (ra_ring_bwd) of the 1M-token share, rank 7: one
+    warm-up, then `reps` timed runs. Counted work: 10*d FLOPs per visible
+    pair per query head (S = q k^T recomputed, dP = dO v^T, dV = P^T dO,
+    dK = dS^T q, dQ = dS k)."""
+    res = {}
+    tot_f = tot_ms = 0.0
+    for layout in layouts:
+        w = workloads.prepare("c4", layout, 7, device=dev)
+        setup_ring(w, dev)
+        ring_call(w, w["out"], w["lse"], w["ws"])
+        g = torch.Generator(device=dev).manual_seed(11)
+        dout = torch.randn(w["q"].shape, generator=g, device=dev).to(w["q"].dtype)
+        c = w["cfg"]
+        b, lq, hq, d = w["q"].shape
+        dq = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev)
+        dk = torch.zeros(w["k"].shape, dtype=torch.float32, device=dev)
+        dv = torch.zeros_like(dk)
+        prob = B.make_problem(dtype=w["q"].dtype, batch=b, hq=hq, hkv=w["k"].shape[3], head_dim=d,
+                              q_len=lq, kv_len=w["k"].shape[2], n_ring=c["n_ring"], rank=7,
+                              causal=c["causal"], layout=layout)
+        ws = torch.empty(B.ra_ring_bwd_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+
+        def run():
+            B.ra_ring_bwd(w["q"], w["k"], w["v"], w["out"], dout, w["lse"], n_ring=c["n_ring"],
+                          causal=c["causal"], layout=layout, rank=7, dq=dq, dk=dk, dv=dv,
+                          workspace=ws)
+
+        run()
+        torch.cuda.synchronize()
+        ms = min(timed(run) for _ in range(reps))
+        flops = 10.0 * d * hq * b * workloads.visible_pairs(layout, c["causal"], c["n_ring"], 7,
+                                                            c["block"])
+        res[layout] = dict(ms=round(ms, 3), tflops=round(flops / (ms / 1e3) / 1e12, 2),
+                           counted_flops=flops)
+        tot_f += flops
+        tot_ms += ms
+        del w, dout, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        log(f"[bench] backward {layout} done")
+    res["tflops"] = round(tot_f / (tot_ms / 1e3) / 1e12, 2)
+    res["pct_bf16_peak"] = round(100 * res["tflops"] / PEAK_BF16_TFLOPS, 2)
+    res["note"] = ("ra_ring_bwd of the same share (dq written, dk/dv addends of all 8 blocks); "
+                   "10*d FLOPs per visible pair; not part of value")
+    return res
+
+
 def load_counters(src_hash):
     """HBM traffic per attention launch from committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
@@ -264,6 +311,9 @@ def main():
                     help="before timing, one device copy of this size (counter calibration)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the timed steps (for profiler runs)")
+    ap.add_argument("--skip-backward", action="store_true", help="no backward leg")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the backward leg (kernel-trace runs of the backward kernels)")
     ap.add_argument("--skip-aux", action="store_true",
                     help="no 8192-token overlap and no widened leg, so that every attention "
                          "launch has the headline workload's shape (kernel-trace runs)")
@@ -279,6 +329,9 @@ def main():
     B.lib()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.backward_only:
+        print(json.dumps({"backward": backward_leg(dev, ["contiguous", "striped"])}), flush=True)
+        return
 
     c = synth.CONFIGS[args.workload]
     layouts = args.layouts.split(",") if args.layouts else list(c["layouts"])
@@ -410,6 +463,8 @@ def main():
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
         log("[bench] merge leg done")
+        if args.workload == "c4" and not args.skip_aux and not args.skip_backward:
+            result["backward"] = backward_leg(dev, layouts)
         if args.workload == "c4" and not args.skip_aux:
             result["widened"] = dict(
                 note=("same 1M-token causal share, rank 7: zigzag layout, and the sequence "

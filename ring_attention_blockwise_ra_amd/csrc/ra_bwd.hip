@@ -444,86 +444,111 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)slot_s(t), 4, 0, 0);
   };
 
+  // per row tile: does any key of this wave meet a visible row, and do some
+  // of its pairs need the element mask
+  auto active = [&](int t) {
+    const int a_hi = (min(t * kRT + kRT, rows_total) - 1) / p.group;
+    return kw_lo < (int)key_end(geom, a_hi, kv_len);
+  };
+  auto needs_mask = [&](int t) {
+    const int a_lo = (t * kRT) / p.group;
+    return !(kw_lo + 31 < (int)key_end(geom, a_lo, kv_len)) || t * kRT + kRT > rows_total;
+  };
+  // S = Q K^T and dP = dO V^T of row tile t (A operands: Q / dO rows in LDS)
+  auto scores = [&](int t, f32x16& s, f32x16& dp) {
+    const char* sQ = slot_q(t);
+    const char* sO = slot_o(t);
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + qoff[k]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[k], k == 0 ? f32x16{} : s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sO + qoff[k]);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[k], k == 0 ? f32x16{} : dp, 0, 0, 0);
+    }
+  };
+  // P and dS of row tile t as bf16 B operands; element i of this lane is
+  // row 8*(i/4) + 4*half + i%4 of the tile
+  auto weights = [&](int t, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+    const bool mask = needs_mask(t);
+    if (mask && half == 0) {
+      const int rho = t * kRT + col;
+      elim[col] = rho < rows_total ? (int)key_end(geom, rho / p.group, kv_len) : 0;
+    }
+    const float* st = slot_s(t);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f32x8 p8, d8;
+#pragma unroll
+      for (int hq4 = 0; hq4 < 2; ++hq4) {
+        const int rbase = 8 * (2 * c + hq4) + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + rbase);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rbase);
+        u32x4 e4 = {0u, 0u, 0u, 0u};
+        if (mask) e4 = *reinterpret_cast<const u32x4*>(elim + rbase);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * c + 4 * hq4 + e;
+          float pv = fast_exp2(__builtin_fmaf(s[i], sl2, -lse_to_log2(l4[e])));
+          if (mask && kmy >= (int)e4[e]) pv = 0.f;  // also rows past the end (limit 0)
+          p8[4 * hq4 + e] = pv;
+          d8[4 * hq4 + e] = pv * (dp[i] - d4[e]);
+        }
+      }
+      pb[c] = __builtin_convertvector(p8, bf16x8);
+      dsb[c] = __builtin_convertvector(d8, bf16x8);
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS (A operands by transposed LDS reads)
+  auto accumulate = [&](int t, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
+    const char* sQ = slot_q(t);
+    const char* sO = slot_o(t);
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int db = j >> 1, c = j & 1;
+      const s16x4 olo = lds_read_tr16(sO + voff[db] + (c * 16) * R::ROWB);
+      const s16x4 ohi = lds_read_tr16(sO + voff8[db] + (c * 16) * R::ROWB);
+      const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+      dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[c], dva[db], 0, 0, 0);
+      const s16x4 qlo = lds_read_tr16(sQ + voff[db] + (c * 16) * R::ROWB);
+      const s16x4 qhi = lds_read_tr16(sQ + voff8[db] + (c * 16) * R::ROWB);
+      const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[c], dka[db], 0, 0, 0);
+    }
+  };
+  // Step t: the weights of tile t (VALU) run beside the MFMAs of tile t+1's
+  // scores, which do not depend on them; then tile t's accumulation.
+  auto step = [&](int t, const f32x16& s_cur, const f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt) {
+    issue(t + 3);
+    const bool act = active(t);
+    bf16x8 pb[2], dsb[2];
+    if (act) weights(t, s_cur, dp_cur, pb, dsb);
+    if (t + 1 < n_rt && active(t + 1)) scores(t + 1, s_nxt, dp_nxt);
+    if (act) accumulate(t, pb, dsb);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
+  };
+
   if (t_first < n_rt) {
-    // Ring of kRowSlots row tiles, loads three tiles ahead; step t issues
-    // tile t+3 into the slot of tile t-1 (read before the barrier closing
-    // step t-1) and ends once tile t+1 has landed (two tiles of its own loads
-    // in flight at most). Tiles past the end load clamped rows, never used.
+    // Ring of kRowSlots row tiles, loads three tiles ahead. Step t reads
+    // tiles t and t+1; it issues tile t+3 into the slot of tile t-1 (read
+    // before the barrier closing step t-1) and ends once tile t+2 has landed
+    // (one tile of its own loads in flight at most). Tiles past the end load
+    // clamped rows and are never read.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     issue(t_first);
     issue(t_first + 1);
     issue(t_first + 2);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
-    for (int t = t_first; t < n_rt; ++t) {
-      issue(t + 3);
-      const int a_lo = (t * kRT) / p.group;
-      const int a_hi = (min(t * kRT + kRT, rows_total) - 1) / p.group;
-      const int e_lo = (int)key_end(geom, a_lo, kv_len);
-      const int e_hi = (int)key_end(geom, a_hi, kv_len);
-      if (kw_lo < e_hi) {  // some key of this wave is visible to some row
-        const bool need_mask = !(kw_lo + 31 < e_lo);
-        if (need_mask && half == 0) {
-          const int rho = t * kRT + col;
-          elim[col] = rho < rows_total ? (int)key_end(geom, rho / p.group, kv_len) : 0;
-        }
-        const char* sQ = slot_q(t);
-        const char* sO = slot_o(t);
-        const float* st = slot_s(t);
-        f32x16 s, dp;
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + qoff[k]);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[k], k == 0 ? f32x16{} : s, 0, 0, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sO + qoff[k]);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[k], k == 0 ? f32x16{} : dp, 0, 0, 0);
-        }
-        // element i of this lane: row 8*(i/4) + 4*half + i%4 of the tile
-        bf16x8 pb[2], dsb[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          f32x8 p8, d8;
-#pragma unroll
-          for (int hq4 = 0; hq4 < 2; ++hq4) {
-            const int rbase = 8 * (2 * c + hq4) + 4 * half;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + rbase);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rbase);
-            int e4[4] = {kv_len, kv_len, kv_len, kv_len};
-            if (need_mask) {
-              const u32x4 x = *reinterpret_cast<const u32x4*>(elim + rbase);
-              e4[0] = (int)x[0]; e4[1] = (int)x[1]; e4[2] = (int)x[2]; e4[3] = (int)x[3];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 8 * c + 4 * hq4 + e;
-              const bool rok = t * kRT + rbase + e < rows_total;
-              const float l2 = rok ? lse_to_log2(l4[e]) : kPosInf;
-              float pv = fast_exp2(__builtin_fmaf(s[i], sl2, -l2));
-              if (kmy >= e4[e]) pv = 0.f;
-              p8[4 * hq4 + e] = pv;
-              d8[4 * hq4 + e] = pv * (dp[i] - (rok ? d4[e] : 0.f));
-            }
-          }
-          pb[c] = __builtin_convertvector(p8, bf16x8);
-          dsb[c] = __builtin_convertvector(d8, bf16x8);
-        }
-#pragma unroll
-        for (int j = 0; j < 2 * DB; ++j) {
-          const int db = j >> 1, c = j & 1;
-          const s16x4 olo = lds_read_tr16(sO + voff[db] + (c * 16) * R::ROWB);
-          const s16x4 ohi = lds_read_tr16(sO + voff8[db] + (c * 16) * R::ROWB);
-          const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[c], dva[db], 0, 0, 0);
-          const s16x4 qlo = lds_read_tr16(sQ + voff[db] + (c * 16) * R::ROWB);
-          const s16x4 qhi = lds_read_tr16(sQ + voff8[db] + (c * 16) * R::ROWB);
-          const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[c], dka[db], 0, 0, 0);
-        }
-      }
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
+    f32x16 sA, dA, sB, dB;
+    if (active(t_first)) scores(t_first, sA, dA);
+    int t = t_first;
+    for (; t + 1 < n_rt; t += 2) {
+      step(t, sA, dA, sB, dB);
+      step(t + 1, sB, dB, sA, dA);
     }
+    if (t < n_rt) step(t, sA, dA, sB, dB);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
