@@ -32,7 +32,10 @@ Pages cited (by title and section; the pages are web text on Ring Attention):
        sequences of different lengths is named as a difficulty; and section
        "Blockwise Backward": the backward pass does not keep the attention
        matrix but recomputes the attention statistics, each device only on
-       the K/V block visiting it.
+       the K/V block visiting it; and section "RoPE va Position Embedding":
+       a key block arriving from another device must be rotated by the angle
+       m*theta of each token's own position m, carried as position metadata
+       with the block.
 
 Conventions
   * Tensors are [batch, seq, heads, head_dim] (the shape convention of the
@@ -405,6 +408,62 @@ def ring_share_literal(q_share, k_blocks, v_blocks, rank: int, n_ring: int,
                 num[b, :, h, :] += e @ vb[b, :, g, :]
                 den[b, :, h] += e.sum(axis=1)
     return num / den[..., None]
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding ([TS] "RoPE va Position Embedding").
+#
+# The page fixes only that a token at position m is rotated by the angle
+# m*theta. The plain reading, the rotary embedding's usual form: head
+# dimensions pair up as (2i, 2i+1), pair i turns by m * theta_i with
+# theta_i = base^(-2i/d) (base 10000 by default), counter-clockwise:
+#   (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a),  a = m theta_i.
+# q and k are rotated (v is not); the scores then depend on positions only
+# through m - n. Positions are global positions (packed sequences: positions
+# within the sequence).
+# --------------------------------------------------------------------------
+
+def rope_angles(pos, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """[len(pos), head_dim/2] angles m * base^(-2i/d) in float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * i / head_dim)
+    return np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+
+
+def rope_rotate(x, pos, base: float = 10000.0, inverse: bool = False) -> np.ndarray:
+    """Rotate x [B, L, H, d] (token t at position pos[t]) pairwise as above;
+    inverse=True turns by -a (the transpose, used on gradients).
+    Pinned by: complex-number multiplication, a hand-worked d=4 case,
+    orthogonality, the relative-position property."""
+    x = _f64(x)
+    a = rope_angles(pos, x.shape[-1], base)
+    if inverse:
+        a = -a
+    c, s_ = np.cos(a)[None, :, None, :], np.sin(a)[None, :, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * c - x1 * s_
+    y[..., 1::2] = x0 * s_ + x1 * c
+    return y
+
+
+def ring_share_rope(q_share, k_blocks, v_blocks, rank: int, n_ring: int, layout: str,
+                    causal: bool, base: float = 10000.0, scale: float | None = None, seqlens=None):
+    """O2 with rotary embedding applied on arrival: the local queries are
+    rotated by their own positions once, and every arriving key block by the
+    positions of its tokens (the block's position metadata) before its
+    partial is formed. Returns (out, lse) as ring_share.
+    Pinned by: equality with plain attention on globally rotated q, k."""
+    lq, lk = q_share.shape[1], k_blocks.shape[2]
+    if seqlens is None:
+        qp = global_positions(layout, n_ring, rank, lq)
+        kps = [global_positions(layout, n_ring, j, lk) for j in range(n_ring)]
+    else:
+        qp = varlen_positions(layout, n_ring, rank, seqlens)[1]
+        kps = [varlen_positions(layout, n_ring, j, seqlens)[1] for j in range(n_ring)]
+    qr = rope_rotate(q_share, qp, base)
+    kr = np.stack([rope_rotate(k_blocks[j], kps[j], base) for j in range(n_ring)])
+    return ring_share(qr, kr, v_blocks, rank, n_ring, layout, causal, scale, seqlens=seqlens)
 
 
 # --------------------------------------------------------------------------

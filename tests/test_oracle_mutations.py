@@ -366,3 +366,83 @@ def test_backward_pins_catch_mutant(name, monkeypatch):
     monkeypatch.setattr(orc, attr, fn)
     with np.errstate(all="ignore"):
         assert not _bwd_pins_hold(), f"mutant {name} survived the pins"
+
+
+# ---------------------------------------------------------------- rope ------
+from tests.test_oracle_rope import _rope_complex  # noqa: E402
+
+_orig_rope = orc.rope_rotate
+_orig_angles = orc.rope_angles
+_orig_ring_rope = orc.ring_share_rope
+
+
+def _rope_pins_hold() -> bool:
+    try:
+        x = np.array([1.0, 0.0, 0.0, 1.0]).reshape(1, 1, 1, 4)
+        want = [math.cos(3), math.sin(3), -math.sin(0.3), math.cos(0.3)]
+        if not np.allclose(orc.rope_rotate(x, [3], base=100.0).reshape(-1), want, atol=1e-12):
+            return False
+        xr, _, _ = _rand(1, 1, 5, 2, 1, 16)
+        pos = np.array([0, 3, 77, 4096, 99999])
+        if not np.allclose(orc.rope_rotate(xr, pos), _rope_complex(xr, pos, 10000.0), atol=1e-10):
+            return False
+        n, blen = 3, 4
+        q, k, v = _rand(6, 1, n * blen, 2, 1, 16)
+        gp = np.arange(n * blen)
+        ref = _sdpa64(_rope_complex(q, gp, 10000.0), _rope_complex(k, gp, 10000.0), v, True)
+        for layout in ("contiguous", "striped", "zigzag"):
+            kb, vb = _blocks_from_global(k, layout, n), _blocks_from_global(v, layout, n)
+            for r in range(n):
+                rows = _share_rows(layout, n, r, blen)
+                out, _ = orc.ring_share_rope(q[:, rows], kb, vb, r, n, layout, True)
+                if not np.allclose(out, ref[:, rows], atol=1e-10):
+                    return False
+        return True
+    except (ValueError, IndexError, FloatingPointError):
+        return False
+
+
+def test_unmutated_rope_passes_battery():
+    assert _rope_pins_hold()
+
+
+def _mut_rope_half_split(x, pos, base=10000.0, inverse=False):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    inv = np.argsort(perm)
+    return _orig_rope(x[..., inv], pos, base, inverse)[..., perm]
+
+
+def _mut_rope_clockwise(x, pos, base=10000.0, inverse=False):
+    return _orig_rope(x, pos, base, not inverse)
+
+
+def _mut_rope_angles_exponent(pos, head_dim, base=10000.0):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.asarray(pos, dtype=np.float64)[:, None] * (base ** (-i / head_dim))[None, :]
+
+
+def _mut_ring_rope_local_positions(q_share, k_blocks, v_blocks, rank, n_ring, layout, causal,
+                                   base=10000.0, scale=None, seqlens=None):
+    lq = q_share.shape[1]
+    qr = _orig_rope(q_share, np.arange(lq), base)
+    kr = np.stack([_orig_rope(k_blocks[j], np.arange(k_blocks.shape[2]), base)
+                   for j in range(n_ring)])
+    return orc.ring_share(qr, kr, v_blocks, rank, n_ring, layout, causal, scale, seqlens=seqlens)
+
+
+ROPE_MUTANTS = {
+    "rope_half_split_pairs": ("rope_rotate", _mut_rope_half_split),
+    "rope_clockwise": ("rope_rotate", _mut_rope_clockwise),
+    "rope_frequency_exponent": ("rope_angles", _mut_rope_angles_exponent),
+    "rope_local_positions": ("ring_share_rope", _mut_ring_rope_local_positions),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTANTS))
+def test_rope_pins_catch_mutant(name, monkeypatch):
+    attr, fn = ROPE_MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    with np.errstate(all="ignore"):
+        assert not _rope_pins_hold(), f"mutant {name} survived the pins"
