@@ -107,6 +107,18 @@ typedef struct {
    * query's within it). At most RA_MAX_SEQS sequences. */
   int32_t n_seqs;
   const int64_t* cu_seqlens;
+  /* Rotary position embedding applied on arrival ([TS] "RoPE va Position
+   * Embedding": an arriving key block is rotated by m*theta for each token's
+   * own position m, known from the block's position metadata). 0: none.
+   * > 0: the base of theta_i = rope_theta^(-2i/head_dim); ra_ring_fwd and
+   * ra_ring_bwd then rotate the local queries once and every K block while
+   * staging it (head-dim pairs (2i, 2i+1) turn by pos * theta_i,
+   * counter-clockwise; pos is the token's global position, within its
+   * sequence when packed), and ra_ring_bwd returns gradients with respect
+   * to the unrotated q and k. The block-level entry points ignore it (they
+   * take already rotated inputs, see ra_rope_apply). Negative or non-finite
+   * values are invalid. */
+  float rope_theta;
 } ra_problem;
 
 /*
@@ -154,7 +166,7 @@ ra_status ra_finalize(int64_t rows, int32_t head_dim, const float* m, const floa
 
 /* Workspace bytes ra_ring_fwd needs for this problem (0 on invalid input):
  * two staging buffers for K and two for V, one partial (m, l, acc) and the
- * running m and l. */
+ * running m and l (with rope_theta > 0 also the rotated queries). */
 size_t ra_ring_workspace_bytes(const ra_problem* prob);
 
 /*
@@ -174,6 +186,8 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob);
  * place; for s >= 1 block j is first copied into staging buffer s % 2 on
  * copy_stream while step s-1 computes on compute_stream (events order the
  * copy after the last read of that buffer, and the compute after the copy).
+ * With rope_theta > 0 every step's K block, the local one included, is
+ * staged and rotated on the way (V is copied as is).
  * Blocks whose every pair is masked are still staged but not computed.
  * copy_stream may be NULL or equal to compute_stream: copies then run in
  * order on compute_stream. On return all work is enqueued; everything
@@ -240,7 +254,8 @@ ra_status ra_block_attn_bwd(const ra_problem* prob, int32_t kv_block_j, const vo
                             void* hip_stream);
 
 /* Workspace bytes ra_ring_bwd needs (0 on invalid input): two staging
- * buffers for K and two for V, and D. */
+ * buffers for K and two for V, and D (with rope_theta > 0 also the rotated
+ * queries and one float32 block for the rotated dK addend). */
 size_t ra_ring_bwd_workspace_bytes(const ra_problem* prob);
 
 /*
@@ -262,6 +277,24 @@ ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, cons
                       const float* out, const void* dout, const float* lse, float* dq,
                       float* dk, float* dv, void* workspace, size_t workspace_bytes,
                       void* compute_stream, void* copy_stream);
+
+/* Which tokens ra_rope_apply rotates: the local queries (block = rank,
+ * q_len tokens) or the keys of block j (kv_len tokens). */
+typedef enum { RA_ROPE_QUERIES = 0, RA_ROPE_KEYS = 1 } ra_rope_target;
+
+/*
+ * Rotary embedding of one block-shaped tensor [batch, len, heads, head_dim]
+ * ([TS] "RoPE va Position Embedding"), with the positions the problem's
+ * layout and packing give its tokens, and base prob->rope_theta (which must
+ * be > 0). inverse turns by the negative angles (the transpose: it maps a
+ * gradient with respect to rotated inputs to one with respect to unrotated
+ * inputs). x has in_dtype, y out_dtype (RA_BF16 or RA_F32); y may equal x
+ * (same dtype) but must not partially overlap it. accumulate = 1 adds the
+ * result into y (out_dtype RA_F32 only).
+ */
+ra_status ra_rope_apply(const ra_problem* prob, int32_t target, int32_t block_j, int32_t heads,
+                        int32_t in_dtype, const void* x, int32_t out_dtype, void* y,
+                        int32_t inverse, int32_t accumulate, void* hip_stream);
 
 /* Thread-local message describing the last failure on this thread. */
 const char* ra_last_error(void);

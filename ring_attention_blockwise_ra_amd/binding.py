@@ -25,6 +25,7 @@ RA_F32, RA_BF16 = 0, 1
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
 RA_TILE_SKIP, RA_TILE_PARTIAL, RA_TILE_FULL = 0, 1, 2
 RA_MAX_SEQS = 256
+RA_ROPE_QUERIES, RA_ROPE_KEYS = 0, 1
 
 _LAYOUT = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED,
            "zigzag": RA_LAYOUT_ZIGZAG, RA_LAYOUT_CONTIGUOUS: RA_LAYOUT_CONTIGUOUS,
@@ -35,7 +36,7 @@ EXPORTED = (
     "ra_block_attn_partial", "ra_merge_partials", "ra_finalize", "ra_ring_workspace_bytes",
     "ra_ring_fwd", "ra_tile_class_host", "ra_tile_classes_host", "ra_tile_classes_device",
     "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
-    "ra_last_error",
+    "ra_rope_apply", "ra_last_error",
 )
 
 
@@ -46,6 +47,7 @@ class RaProblem(ctypes.Structure):
         ("kv_len", ctypes.c_int64), ("n_ring", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("layout", ctypes.c_int32), ("scale", ctypes.c_float),
         ("n_seqs", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
+        ("rope_theta", ctypes.c_float),
     ]
     # keeps the host cu_seqlens array alive as long as the problem
     _keep = None
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
             L.ra_ring_bwd_workspace_bytes.restype = ctypes.c_size_t
             L.ra_ring_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
             L.ra_ring_bwd.restype = I32
+            L.ra_rope_apply.argtypes = [PP, I32, I32, I32, I32, P, I32, P, I32, I32, P]
+            L.ra_rope_apply.restype = I32
             L.ra_last_error.argtypes = []
             L.ra_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -120,15 +124,16 @@ def _stream(s, device) -> ctypes.c_void_p:
 
 
 def make_problem(*, dtype, batch, hq, hkv, head_dim, q_len, kv_len, n_ring, rank, causal,
-                 layout, scale=None, cu_seqlens=None) -> RaProblem:
+                 layout, scale=None, cu_seqlens=None, rope_theta=0.0) -> RaProblem:
     """cu_seqlens: offsets [n_seqs + 1] of packed sequences in the global
-    packed sequence (host list/array/tensor), or None."""
+    packed sequence (host list/array/tensor), or None. rope_theta: base of
+    the rotary embedding the ring applies on arrival (0: none)."""
     p = RaProblem(
         dtype=_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
         batch=int(batch), hq=int(hq), hkv=int(hkv), head_dim=int(head_dim),
         q_len=int(q_len), kv_len=int(kv_len), n_ring=int(n_ring), rank=int(rank),
         causal=int(bool(causal)), layout=_LAYOUT[layout],
-        scale=float(scale) if scale is not None else 0.0)
+        scale=float(scale) if scale is not None else 0.0, rope_theta=float(rope_theta))
     if cu_seqlens is not None:
         if isinstance(cu_seqlens, torch.Tensor):
             cu_seqlens = cu_seqlens.detach().cpu().numpy()
@@ -154,7 +159,7 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens=None):
+def _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens=None, rope_theta=0.0):
     if q.dim() != 4 or k.dim() < 4:
         raise ValueError("q must be [batch, q_len, hq, d]; k, v [.., batch, kv_len, hkv, d]")
     if q.dtype not in _DTYPE:
@@ -163,7 +168,7 @@ def _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens=None):
     lk, hkv = k.shape[-3], k.shape[-2]
     return make_problem(dtype=q.dtype, batch=b, hq=hq, hkv=hkv, head_dim=d, q_len=lq, kv_len=lk,
                         n_ring=n_ring, rank=rank, causal=causal, layout=layout, scale=scale,
-                        cu_seqlens=cu_seqlens)
+                        cu_seqlens=cu_seqlens, rope_theta=rope_theta)
 
 
 def ra_block_attn_partial(q, k, v, kv_block_j: int, *, n_ring: int, rank: int, causal: bool,
@@ -234,9 +239,10 @@ def ra_ring_workspace_bytes(prob: RaProblem) -> int:
 
 def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank: int = None,
                 scale=None, out=None, lse=None, want_lse=True, workspace=None,
-                compute_stream=None, copy_stream="auto", cu_seqlens=None):
+                compute_stream=None, copy_stream="auto", cu_seqlens=None, rope_theta=0.0):
     """One device's share: q [b, lq, hq, d]; k, v [n_ring, b, lk, hkv, d].
     cu_seqlens: packed sequences (batch 1), global offsets [n_seqs + 1].
+    rope_theta > 0: rotary embedding applied on arrival (q and k unrotated).
 
     Returns (out fp32 [b, lq, hq, d], lse fp32 [b, lq, hq] or None).
     copy_stream: "auto" (a dedicated side stream per device), None (copies
@@ -245,7 +251,7 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
     if rank is None:
         rank = n_ring - 1
     _need(q, "q")
-    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens, rope_theta)
     b, lq, hq, d = q.shape
     dev = q.device
     _need(k, "k", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
@@ -325,14 +331,14 @@ def ra_ring_bwd_workspace_bytes(prob: RaProblem) -> int:
 
 def ra_ring_bwd(q, k, v, out, dout, lse, *, n_ring: int, causal: bool, layout="contiguous",
                 rank: int = None, scale=None, dq=None, dk=None, dv=None, workspace=None,
-                compute_stream=None, copy_stream="auto", cu_seqlens=None):
+                compute_stream=None, copy_stream="auto", cu_seqlens=None, rope_theta=0.0):
     """Backward of one device's share: returns (dq, dk, dv). dq is written;
     this share's addends are ADDED to dk, dv [n_ring, b, lk, hkv, d] (new
     zeroed tensors when not given)."""
     if rank is None:
         rank = n_ring - 1
     _need(q, "q")
-    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens, rope_theta)
     b, lq, hq, d = q.shape
     dev = q.device
     kshape = (n_ring, b, prob.kv_len, prob.hkv, d)
@@ -364,6 +370,27 @@ def ra_ring_bwd(q, k, v, out, dout, lse, *, n_ring: int, causal: bool, layout="c
                                  _ptr(workspace), workspace.numel(),
                                  ctypes.c_void_p(cs.cuda_stream), xs))
     return dq, dk, dv
+
+
+def ra_rope_apply(x, prob: RaProblem, *, target="keys", block_j: int = 0, out=None,
+                  out_dtype=None, inverse=False, accumulate=False, stream=None):
+    """Rotary embedding of x [b, len, heads, d] with the positions of block
+    block_j's keys (target="keys") or of the local queries ("queries")."""
+    _need(x, "x")
+    if x.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = torch.zeros(x.shape, dtype=out_dtype, device=x.device) if accumulate else \
+            torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _need(out, "out", out_dtype, x.shape, x.device)
+    tgt = RA_ROPE_QUERIES if target == "queries" else RA_ROPE_KEYS
+    with torch.cuda.device(x.device):
+        _check(lib().ra_rope_apply(ctypes.byref(prob), tgt, int(block_j), int(x.shape[2]),
+                                   _DTYPE[x.dtype], _ptr(x), _DTYPE[out_dtype], _ptr(out),
+                                   int(bool(inverse)), int(bool(accumulate)),
+                                   _stream(stream, x.device)))
+    return out
 
 
 _side = {}

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libra_amd.so")
-SOURCES = ["ra_kernels.hip", "ra_bwd.hip", "ra_api.hip"]
+SOURCES = ["ra_kernels.hip", "ra_bwd.hip", "ra_rope.hip", "ra_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -119,6 +119,8 @@ ra_status validate_problem(const ra_problem* p, Shape* s) {
                 (long long)p->q_len, (long long)p->kv_len);
   if (isnan(p->scale) || isinf(p->scale))
     return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  if (isnan(p->rope_theta) || isinf(p->rope_theta) || p->rope_theta < 0.f)
+    return fail(RA_ERR_INVALID_ARG, "rope_theta must be finite and >= 0");
   // the kernels address one batch row of a KV block with 32-bit offsets
   if ((int64_t)p->kv_len * p->hkv * p->head_dim > INT32_MAX)
     return fail(RA_ERR_UNSUPPORTED, "kv_len*hkv*head_dim exceeds 2^31-1 elements");
@@ -239,6 +241,32 @@ ra::BwdParams make_bwd_params(const ra_problem* p, const Shape& s, int32_t j, co
   return a;
 }
 
+// Rotary embedding of block `block` (queries of the share when block ==
+// rank and queries is set): tokens len, heads heads.
+ra::RopeParams make_rope(const ra_problem* p, const Shape& s, bool queries, int32_t block,
+                         int32_t heads, bool in_bf16, const void* x, bool out_bf16, void* y,
+                         bool inverse, bool accumulate) {
+  ra::RopeParams r{};
+  r.x = x;
+  r.y = y;
+  r.in_bf16 = in_bf16;
+  r.out_bf16 = out_bf16;
+  r.accumulate = accumulate;
+  r.inverse = inverse;
+  r.batch = p->batch;
+  r.len = (int32_t)(queries ? p->q_len : p->kv_len);
+  r.heads = heads;
+  r.head_dim = p->head_dim;
+  r.layout = p->layout;
+  r.n_ring = p->n_ring;
+  r.block = block;
+  r.packed = s.packed;
+  r.seg = s.seg;
+  for (int i = 0; i < p->head_dim / 2 && i < 64; ++i)
+    r.inv_freq[i] = pow((double)p->rope_theta, -2.0 * i / p->head_dim);
+  return r;
+}
+
 // Enqueue one block's backward addends (nothing for a block with no visible
 // pair or no keys: its addends are zero).
 ra_status enqueue_bwd(const ra_problem* p, const Shape& s, int32_t j, const void* q, const void* k,
@@ -255,13 +283,14 @@ ra_status enqueue_bwd(const ra_problem* p, const Shape& s, int32_t j, const void
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct BwdWsLayout {
-  size_t stage_k[2], stage_v[2], delta, total;
+  size_t stage_k[2], stage_v[2], delta, qrot, dktmp, total;
 };
 
 BwdWsLayout bwd_ws_layout(const ra_problem* p, const Shape& s) {
   BwdWsLayout w{};
   const size_t blk = align256((size_t)s.kv_elems * s.elem);
-  const bool staged = p->n_ring > 1;
+  const bool rope = p->rope_theta > 0.f;
+  const bool staged = p->n_ring > 1 || rope;
   size_t off = 0;
   for (int i = 0; i < 2; ++i) {
     w.stage_k[i] = off;
@@ -271,13 +300,19 @@ BwdWsLayout bwd_ws_layout(const ra_problem* p, const Shape& s) {
   }
   w.delta = off;
   off += align256((size_t)s.rows * 4);
+  w.qrot = off;
+  off += rope ? align256((size_t)s.q_elems * s.elem) : 0;
+  w.dktmp = off;
+  off += rope ? align256((size_t)s.kv_elems * 4) : 0;
   w.total = off;
   return w;
 }
 
 struct WsLayout {
-  size_t stage_k[2], stage_v[2], pm, pl, pacc, rm, rl, total;
+  size_t stage_k[2], stage_v[2], pm, pl, pacc, rm, rl, qrot, total;
 };
+
+bool rope_on(const ra_problem* p) { return p->rope_theta > 0.f; }
 
 WsLayout ws_layout(const ra_problem* p, const Shape& s) {
   WsLayout w{};
@@ -285,7 +320,7 @@ WsLayout ws_layout(const ra_problem* p, const Shape& s) {
   const size_t rowb = align256((size_t)s.rows * 4);
   const size_t accb = align256((size_t)s.q_elems * 4);
   size_t off = 0;
-  const bool staged = p->n_ring > 1;
+  const bool staged = p->n_ring > 1 || rope_on(p);
   for (int i = 0; i < 2; ++i) {
     w.stage_k[i] = off;
     off += staged ? blk : 0;
@@ -294,9 +329,10 @@ WsLayout ws_layout(const ra_problem* p, const Shape& s) {
   }
   w.pm = off; off += rowb;
   w.pl = off; off += rowb;
-  w.pacc = off; off += staged ? accb : 0;
+  w.pacc = off; off += p->n_ring > 1 ? accb : 0;
   w.rm = off; off += rowb;
   w.rl = off; off += rowb;
+  w.qrot = off; off += rope_on(p) ? align256((size_t)s.q_elems * s.elem) : 0;
   w.total = off;
   return w;
 }
@@ -337,6 +373,91 @@ ra_status init_events(DeviceEvents* de) {
   de->ready = true;
   return RA_OK;
 }
+
+// The ring's K/V blocks on their way into the two staging buffers. Step s
+// uses block (rank - s) mod N; it reads the block in place unless it is
+// staged (every step s >= 1, and step 0 too with rotary embedding, which
+// rotates K while copying it). Events order each copy after the last reader
+// of its buffer and each step's kernels after the copy that filled theirs.
+struct Stager {
+  const ra_problem* p;
+  const Shape* s;
+  const char* kbase;
+  const char* vbase;
+  size_t blk;
+  char* stage_k[2];
+  char* stage_v[2];
+  DeviceEvents* de;
+  hipStream_t cs, xs;
+  bool sep, rope;
+
+  int block_of(int step) const { return ((p->rank - step) % p->n_ring + p->n_ring) % p->n_ring; }
+  bool staged(int step) const { return rope || step >= 1; }
+
+  ra_status begin() {
+    hipError_t e;
+    if (!sep) return RA_OK;
+    if ((e = hipEventRecord(de->entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(xs, de->entry, 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+    return RA_OK;
+  }
+  ra_status stage(int step) {
+    const int j = block_of(step), b = step % 2;
+    hipStream_t on = sep ? xs : cs;
+    hipError_t e;
+    if (rope) {
+      ra::RopeParams r = make_rope(p, *s, false, j, p->hkv, p->dtype == RA_BF16,
+                                   kbase + (size_t)j * blk, p->dtype == RA_BF16, stage_k[b],
+                                   false, false);
+      e = ra::launch_rope(r, on);
+    } else {
+      e = hipMemcpyAsync(stage_k[b], kbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice, on);
+    }
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice, on);
+    if (e != hipSuccess) return hip_fail(e, "staging copy");
+    if (sep && (e = hipEventRecord(de->copy_done[b], xs)) != hipSuccess)
+      return hip_fail(e, "hipEventRecord");
+    return RA_OK;
+  }
+  // before step `step` computes: bring in the block of step+1 (its buffer
+  // was last read by step-1) and wait for this step's own block
+  ra_status advance(int step, const void** k, const void** v) {
+    hipError_t e;
+    if (step >= 1 && step + 1 < p->n_ring) {
+      if (sep && staged(step - 1) &&
+          (e = hipStreamWaitEvent(xs, de->compute_done[(step - 1) % 2], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      ra_status st = stage(step + 1);
+      if (st != RA_OK) return st;
+    }
+    const int j = block_of(step), b = step % 2;
+    if (!staged(step)) {
+      *k = kbase + (size_t)j * blk;
+      *v = vbase + (size_t)j * blk;
+      return RA_OK;
+    }
+    if (sep && (e = hipStreamWaitEvent(cs, de->copy_done[b], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+    *k = stage_k[b];
+    *v = stage_v[b];
+    return RA_OK;
+  }
+  ra_status done(int step) {
+    hipError_t e;
+    if (sep && staged(step) && (e = hipEventRecord(de->compute_done[step % 2], cs)) != hipSuccess)
+      return hip_fail(e, "hipEventRecord");
+    return RA_OK;
+  }
+  // the first copies: step 0's block (rotary embedding) and step 1's
+  ra_status start() {
+    ra_status st = begin();
+    if (st == RA_OK && rope) st = stage(0);
+    if (st == RA_OK && p->n_ring > 1) st = stage(1);
+    return st;
+  }
+};
 
 }  // namespace
 
@@ -511,67 +632,40 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
     if ((st = init_events(de)) != RA_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
-    const char* kbase = static_cast<const char*>(k);
-    const char* vbase = static_cast<const char*>(v);
-    char* stage_k[2] = {ws + w.stage_k[0], ws + w.stage_k[1]};
-    char* stage_v[2] = {ws + w.stage_v[0], ws + w.stage_v[1]};
     float* pm = reinterpret_cast<float*>(ws + w.pm);
     float* pl = reinterpret_cast<float*>(ws + w.pl);
     float* pacc = reinterpret_cast<float*>(ws + w.pacc);
     float* rm = reinterpret_cast<float*>(ws + w.rm);
     float* rl = reinterpret_cast<float*>(ws + w.rl);
-    auto block_of = [&](int step) { return ((prob->rank - step) % n + n) % n; };
+    Stager sg{prob, &s, static_cast<const char*>(k), static_cast<const char*>(v), blk,
+              {ws + w.stage_k[0], ws + w.stage_k[1]}, {ws + w.stage_v[0], ws + w.stage_v[1]},
+              de, cs, xs, sep, rope_on(prob)};
     hipError_t e;
-    hipStream_t copy_on = sep ? xs : cs;
-
-    if (sep) {
-      if ((e = hipEventRecord(de->entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-      if ((e = hipStreamWaitEvent(xs, de->entry, 0)) != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
+    const void* qx = q;
+    if (sg.rope) {  // the local queries, rotated once by their own positions
+      void* qr = ws + w.qrot;
+      ra::RopeParams r = make_rope(prob, s, true, prob->rank, prob->hq, prob->dtype == RA_BF16, q,
+                                   prob->dtype == RA_BF16, qr, false, false);
+      if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
+      qx = qr;
     }
-    auto stage = [&](int step) -> ra_status {
-      const int j = block_of(step), b = step % 2;
-      hipError_t e2 = hipMemcpyAsync(stage_k[b], kbase + (size_t)j * blk, blk,
-                                     hipMemcpyDeviceToDevice, copy_on);
-      if (e2 == hipSuccess)
-        e2 = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice,
-                            copy_on);
-      if (e2 != hipSuccess) return hip_fail(e2, "staging hipMemcpyAsync");
-      if (sep && (e2 = hipEventRecord(de->copy_done[b], xs)) != hipSuccess)
-        return hip_fail(e2, "hipEventRecord");
-      return RA_OK;
-    };
-
-    // step 0: the local block, read in place, written straight into the
-    // running state (m, l, out)
-    const int j0 = block_of(0);
-    if ((st = enqueue_partial(prob, s, j0, q, kbase + (size_t)j0 * blk, vbase + (size_t)j0 * blk,
-                              rm, rl, out, cs)) != RA_OK)
-      return st;
-    if (n > 1 && (st = stage(1)) != RA_OK) return st;
-
-    for (int step = 1; step < n; ++step) {
-      if (step + 1 < n) {
-        // buffer (step+1)%2 was last read by step-1 (steps >= 1 read staging)
-        if (sep && step - 1 >= 1 &&
-            (e = hipStreamWaitEvent(xs, de->compute_done[(step - 1) % 2], 0)) != hipSuccess)
-          return hip_fail(e, "hipStreamWaitEvent");
-        if ((st = stage(step + 1)) != RA_OK) return st;
+    if ((st = sg.start()) != RA_OK) return st;
+    for (int step = 0; step < n; ++step) {
+      const void *kb = nullptr, *vb = nullptr;
+      if ((st = sg.advance(step, &kb, &vb)) != RA_OK) return st;
+      const int j = sg.block_of(step);
+      if (step == 0) {
+        // the local block's partial is the running state (m, l, out)
+        if ((st = enqueue_partial(prob, s, j, qx, kb, vb, rm, rl, out, cs)) != RA_OK) return st;
+      } else {
+        ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, j);
+        if (g.kind != ra::kNoneVisible && prob->kv_len > 0) {
+          if ((st = enqueue_partial(prob, s, j, qx, kb, vb, pm, pl, pacc, cs)) != RA_OK) return st;
+          e = ra::launch_merge(s.rows, prob->head_dim, rm, rl, out, pm, pl, pacc, rm, rl, out, cs);
+          if (e != hipSuccess) return hip_fail(e, "merge launch");
+        }
       }
-      const int b = step % 2;
-      if (sep && (e = hipStreamWaitEvent(cs, de->copy_done[b], 0)) != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
-      const int j = block_of(step);
-      ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, j);
-      if (g.kind != ra::kNoneVisible && prob->kv_len > 0) {
-        if ((st = enqueue_partial(prob, s, j, q, stage_k[b], stage_v[b], pm, pl, pacc, cs)) !=
-            RA_OK)
-          return st;
-        e = ra::launch_merge(s.rows, prob->head_dim, rm, rl, out, pm, pl, pacc, rm, rl, out, cs);
-        if (e != hipSuccess) return hip_fail(e, "merge launch");
-      }
-      if (sep && (e = hipEventRecord(de->compute_done[b], cs)) != hipSuccess)
-        return hip_fail(e, "hipEventRecord");
+      if ((st = sg.done(step)) != RA_OK) return st;
     }
     e = ra::launch_finalize(s.rows, prob->head_dim, rm, rl, out, lse, cs);
     if (e != hipSuccess) return hip_fail(e, "finalize launch");
@@ -709,60 +803,95 @@ ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, cons
     if ((st = init_events(de)) != RA_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
-    const char* kbase = static_cast<const char*>(k);
-    const char* vbase = static_cast<const char*>(v);
-    char* stage_k[2] = {ws + w.stage_k[0], ws + w.stage_k[1]};
-    char* stage_v[2] = {ws + w.stage_v[0], ws + w.stage_v[1]};
     float* delta = reinterpret_cast<float*>(ws + w.delta);
-    auto block_of = [&](int step) { return ((prob->rank - step) % n + n) % n; };
-    hipError_t e;
-    hipStream_t copy_on = sep ? xs : cs;
-    if (sep) {
-      if ((e = hipEventRecord(de->entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-      if ((e = hipStreamWaitEvent(xs, de->entry, 0)) != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
-    }
-    auto stage = [&](int step) -> ra_status {
-      const int j = block_of(step), b = step % 2;
-      hipError_t e2 = hipMemcpyAsync(stage_k[b], kbase + (size_t)j * blk, blk,
-                                     hipMemcpyDeviceToDevice, copy_on);
-      if (e2 == hipSuccess)
-        e2 = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice,
-                            copy_on);
-      if (e2 != hipSuccess) return hip_fail(e2, "staging hipMemcpyAsync");
-      if (sep && (e2 = hipEventRecord(de->copy_done[b], xs)) != hipSuccess)
-        return hip_fail(e2, "hipEventRecord");
-      return RA_OK;
-    };
+    Stager sg{prob, &s, static_cast<const char*>(k), static_cast<const char*>(v), blk,
+              {ws + w.stage_k[0], ws + w.stage_k[1]}, {ws + w.stage_v[0], ws + w.stage_v[1]},
+              de, cs, xs, sep, rope_on(prob)};
     const size_t kelems = (size_t)s.kv_elems;  // floats per block of dk / dv
+    const bool bf = prob->dtype == RA_BF16;
+    hipError_t e;
 
-    // D for every local row, dq from zero, then the ring
-    e = ra::launch_bwd_delta(s.rows, prob->head_dim, prob->dtype == RA_BF16, out, dout, delta, cs);
+    // D for every local row, dq from zero (the local queries rotated once
+    // with rotary embedding), then the ring
+    e = ra::launch_bwd_delta(s.rows, prob->head_dim, bf, out, dout, delta, cs);
     if (e != hipSuccess) return hip_fail(e, "delta launch");
     e = ra::launch_zero(dq, s.q_elems, cs);
     if (e != hipSuccess) return hip_fail(e, "zero launch");
-    const int j0 = block_of(0);
-    if ((st = enqueue_bwd(prob, s, j0, q, kbase + (size_t)j0 * blk, vbase + (size_t)j0 * blk,
-                          dout, lse, delta, dq, dk + j0 * kelems, dv + j0 * kelems, cs)) != RA_OK)
-      return st;
-    if (n > 1 && (st = stage(1)) != RA_OK) return st;
-    for (int step = 1; step < n; ++step) {
-      if (step + 1 < n) {
-        if (sep && step - 1 >= 1 &&
-            (e = hipStreamWaitEvent(xs, de->compute_done[(step - 1) % 2], 0)) != hipSuccess)
-          return hip_fail(e, "hipStreamWaitEvent");
-        if ((st = stage(step + 1)) != RA_OK) return st;
-      }
-      const int b = step % 2;
-      if (sep && (e = hipStreamWaitEvent(cs, de->copy_done[b], 0)) != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
-      const int j = block_of(step);
-      if ((st = enqueue_bwd(prob, s, j, q, stage_k[b], stage_v[b], dout, lse, delta, dq,
-                            dk + j * kelems, dv + j * kelems, cs)) != RA_OK)
-        return st;
-      if (sep && (e = hipEventRecord(de->compute_done[b], cs)) != hipSuccess)
-        return hip_fail(e, "hipEventRecord");
+    const void* qx = q;
+    float* dktmp = reinterpret_cast<float*>(ws + w.dktmp);
+    if (sg.rope) {
+      void* qr = ws + w.qrot;
+      ra::RopeParams r = make_rope(prob, s, true, prob->rank, prob->hq, bf, q, bf, qr, false, false);
+      if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
+      qx = qr;
     }
+    if ((st = sg.start()) != RA_OK) return st;
+    for (int step = 0; step < n; ++step) {
+      const void *kb = nullptr, *vb = nullptr;
+      if ((st = sg.advance(step, &kb, &vb)) != RA_OK) return st;
+      const int j = sg.block_of(step);
+      if (!sg.rope) {
+        if ((st = enqueue_bwd(prob, s, j, qx, kb, vb, dout, lse, delta, dq, dk + j * kelems,
+                              dv + j * kelems, cs)) != RA_OK)
+          return st;
+      } else {
+        // the dK addend is taken with respect to the rotated keys: form it
+        // in a scratch block, turn it back and add it into dk[j]
+        if ((e = ra::launch_zero(dktmp, s.kv_elems, cs)) != hipSuccess)
+          return hip_fail(e, "zero launch");
+        if ((st = enqueue_bwd(prob, s, j, qx, kb, vb, dout, lse, delta, dq, dktmp,
+                              dv + j * kelems, cs)) != RA_OK)
+          return st;
+        ra::RopeParams r = make_rope(prob, s, false, j, prob->hkv, false, dktmp, false,
+                                     dk + j * kelems, true, true);
+        if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
+      }
+      if ((st = sg.done(step)) != RA_OK) return st;
+    }
+    if (sg.rope) {  // dq with respect to the unrotated queries
+      ra::RopeParams r = make_rope(prob, s, true, prob->rank, prob->hq, false, dq, false, dq, true,
+                                   false);
+      if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
+    }
+    return RA_OK;
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+ra_status ra_rope_apply(const ra_problem* prob, int32_t target, int32_t block_j, int32_t heads,
+                        int32_t in_dtype, const void* x, int32_t out_dtype, void* y,
+                        int32_t inverse, int32_t accumulate, void* hip_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    if (!(prob->rope_theta > 0.f)) return fail(RA_ERR_INVALID_ARG, "rope_theta must be > 0");
+    if (target != RA_ROPE_QUERIES && target != RA_ROPE_KEYS)
+      return fail(RA_ERR_INVALID_ARG, "target %d unknown", target);
+    if (block_j < 0 || block_j >= prob->n_ring)
+      return fail(RA_ERR_INVALID_ARG, "block_j %d out of [0, n_ring=%d)", block_j, prob->n_ring);
+    if (heads < 1) return fail(RA_ERR_INVALID_ARG, "heads %d < 1", heads);
+    if ((in_dtype != RA_F32 && in_dtype != RA_BF16) || (out_dtype != RA_F32 && out_dtype != RA_BF16))
+      return fail(RA_ERR_INVALID_ARG, "dtypes must be RA_F32 or RA_BF16");
+    if (accumulate && out_dtype != RA_F32)
+      return fail(RA_ERR_INVALID_ARG, "accumulate needs a float32 output");
+    const bool queries = target == RA_ROPE_QUERIES;
+    const int64_t len = queries ? prob->q_len : prob->kv_len;
+    const int64_t elems = (int64_t)prob->batch * len * heads * prob->head_dim;
+    if (elems > (int64_t(1) << 40)) return fail(RA_ERR_INVALID_ARG, "tensor too large");
+    const size_t xb = elems * (in_dtype == RA_BF16 ? 2 : 4), yb = elems * (out_dtype == RA_BF16 ? 2 : 4);
+    if ((st = check_ptr(x, xb, "x")) || (st = check_ptr(y, yb, "y"))) return st;
+    if (x != y && overlap(x, xb, y, yb))
+      return fail(RA_ERR_INVALID_ARG, "y partially overlaps x");
+    if (x == y && (in_dtype != out_dtype || accumulate))
+      return fail(RA_ERR_INVALID_ARG, "in place needs equal dtypes and no accumulate");
+    if (elems == 0) return RA_OK;
+    ra::RopeParams r = make_rope(prob, s, queries, queries ? prob->rank : block_j, heads,
+                                 in_dtype == RA_BF16, x, out_dtype == RA_BF16, y, inverse != 0,
+                                 accumulate != 0);
+    hipError_t e = ra::launch_rope(r, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "rope launch");
     return RA_OK;
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");

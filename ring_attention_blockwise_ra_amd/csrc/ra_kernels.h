@@ -72,6 +72,30 @@ hipError_t launch_zero(float* x, int64_t n, hipStream_t stream);
 hipError_t launch_bwd_delta(int64_t rows, int d, int is_bf16, const float* out, const void* dout,
                             float* delta, hipStream_t stream);
 
+// Rotary embedding of a block-shaped tensor [batch, len, heads, head_dim]:
+// token a of block `block` at its global position (within its sequence when
+// packed) turns head-dim pair (2i, 2i+1) by pos * inv_freq[i] (negated when
+// inverse). y may equal x. accumulate: y += rotated x (float32 y only).
+struct RopeParams {
+  const void* x;
+  void* y;
+  int32_t in_bf16;
+  int32_t out_bf16;
+  int32_t accumulate;
+  int32_t inverse;
+  int32_t batch;
+  int32_t len;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t layout;
+  int32_t n_ring;
+  int32_t block;
+  int32_t packed;
+  SegTable seg;
+  double inv_freq[64];  // base^(-2i/head_dim), i < head_dim/2
+};
+hipError_t launch_rope(const RopeParams& p, hipStream_t stream);
+
 // waves: wavefronts per workgroup of the bf16 kernel (4 or 8; 32 rows each).
 hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream);
 

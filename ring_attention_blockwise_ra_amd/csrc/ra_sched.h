@@ -107,6 +107,15 @@ RA_HD bool visible(BlockGeom g, int64_t a, int64_t b, int64_t kv_len) {
   return b < key_end(g, a, kv_len);
 }
 
+// Global position of local token a of block j (len tokens per block, or
+// per block slice of one packed sequence): the layouts above.
+RA_HD int64_t token_position(int32_t layout, int32_t n_ring, int32_t j, int64_t len, int64_t a) {
+  if (layout == 0) return (int64_t)j * len + a;
+  if (layout == 1) return a * n_ring + j;
+  const int64_t h = len / 2;  // zigzag
+  return a < h ? (int64_t)j * h + a : (int64_t)(2 * n_ring - 1 - j) * h + (a - h);
+}
+
 // Segment holding local row a (the last one starting at or before a, so
 // empty segments are passed over).
 RA_HD int32_t segment_of(const SegTable& t, int64_t a) {

@@ -310,3 +310,23 @@ def test_ring_bwd_workspace_and_checks(L):
         == B.RA_ERR_INVALID_ARG
     one = _prob(n_ring=1, rank=0)
     assert L.ra_ring_bwd_workspace_bytes(ctypes.byref(one)) < need  # no staging buffers
+
+
+def test_rope_validation(L):
+    prob = _prob(rope_theta=float("nan"))
+    assert _partial(L, prob) == B.RA_ERR_INVALID_ARG
+    prob = _prob(rope_theta=-1.0)
+    assert _partial(L, prob) == B.RA_ERR_INVALID_ARG
+    p0 = _prob()  # rope_theta 0: ra_rope_apply refuses
+    assert L.ra_rope_apply(ctypes.byref(p0), 1, 0, 2, B.RA_BF16, FAKE, B.RA_BF16, FAKE, 0, 0, None) \
+        == B.RA_ERR_INVALID_ARG
+    p = _prob(rope_theta=10000.0)
+    assert L.ra_rope_apply(ctypes.byref(p), 5, 0, 2, B.RA_BF16, FAKE, B.RA_BF16, FAKE, 0, 0, None) \
+        == B.RA_ERR_INVALID_ARG
+    assert L.ra_rope_apply(ctypes.byref(p), 1, 4, 2, B.RA_BF16, FAKE, B.RA_BF16, FAKE, 0, 0, None) \
+        == B.RA_ERR_INVALID_ARG  # block out of range
+    assert L.ra_rope_apply(ctypes.byref(p), 1, 0, 2, B.RA_BF16, FAKE, B.RA_BF16, FAKE, 0, 1, None) \
+        == B.RA_ERR_INVALID_ARG  # accumulate into bf16
+    assert L.ra_rope_apply(ctypes.byref(p), 1, 0, 2, B.RA_F32, FAKE, B.RA_BF16, FAKE, 0, 0, None) \
+        == B.RA_ERR_INVALID_ARG  # in place with different dtypes
+    assert L.ra_ring_workspace_bytes(ctypes.byref(p)) > L.ra_ring_workspace_bytes(ctypes.byref(_prob()))
