@@ -58,7 +58,8 @@ def ring_call(w, out, lse, ws, copy_stream="auto"):
     c = w["cfg"]
     return B.ra_ring_fwd(w["q"], w["k"], w["v"], n_ring=c["n_ring"], causal=c["causal"],
                          layout=w["layout"], rank=w["rank"], out=out, lse=lse, workspace=ws,
-                         copy_stream=copy_stream, cu_seqlens=w.get("cu_seqlens"))
+                         copy_stream=copy_stream, cu_seqlens=w.get("cu_seqlens"),
+                         rope_theta=w.get("rope_theta", 0.0))
 
 
 def kernel_leg(w):
@@ -217,17 +218,27 @@ def setup_ring(w, dev):
 
 
 def widened_leg(dev, cases, reps=2):
-    """Ring TF/s of the same 1M-token share in the layouts and packings
-    beyond the headline pair (one warm-up, median of `reps`)."""
+    """Ring TF/s of the same 1M-token share in the layouts, packings and
+    with the rotary embedding beyond the headline pair (one warm-up, median
+    of `reps`). A case is (workload, layout, rope_theta)."""
     res = {}
-    for name, layout in cases:
+    for name, layout, theta in cases:
         w = workloads.prepare(name, layout, 7, device=dev)
         setup_ring(w, dev)
+        if theta:
+            c = w["cfg"]
+            b, lq, hq, d = w["q"].shape
+            prob = B.make_problem(dtype=w["q"].dtype, batch=b, hq=hq, hkv=w["k"].shape[3],
+                                  head_dim=d, q_len=lq, kv_len=w["k"].shape[2],
+                                  n_ring=c["n_ring"], rank=7, causal=c["causal"],
+                                  layout=layout, rope_theta=theta)
+            w["ws"] = torch.empty(B.ra_ring_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+        w["rope_theta"] = theta
         ring_call(w, w["out"], w["lse"], w["ws"])
         torch.cuda.synchronize()
         ts = sorted(timed(lambda: ring_call(w, w["out"], w["lse"], w["ws"])) for _ in range(reps))
         ms = ts[len(ts) // 2]
-        key = f"{name}_{layout}"
+        key = f"{name}_{layout}" + ("_rope" if theta else "")
         res[key] = dict(ms=round(ms, 3), tflops=round(w["flops"] / (ms / 1e3) / 1e12, 2),
                         counted_flops=w["flops"],
                         sequences=None if w.get("seqlens") is None else len(w["seqlens"]))
@@ -467,10 +478,12 @@ def main():
             result["backward"] = backward_leg(dev, layouts)
         if args.workload == "c4" and not args.skip_aux:
             result["widened"] = dict(
-                note=("same 1M-token causal share, rank 7: zigzag layout, and the sequence "
-                      "packed from mixed-length documents (c4p) in zigzag and contiguous "
-                      "layouts; not part of value"),
-                **widened_leg(dev, [("c4", "zigzag"), ("c4p", "zigzag"), ("c4p", "contiguous")]))
+                note=("same 1M-token causal share, rank 7: zigzag layout, the sequence packed "
+                      "from mixed-length documents (c4p) in zigzag and contiguous layouts, and "
+                      "zigzag with the rotary embedding applied on arrival (base 500000); not "
+                      "part of value"),
+                **widened_leg(dev, [("c4", "zigzag", 0.0), ("c4p", "zigzag", 0.0),
+                                    ("c4p", "contiguous", 0.0), ("c4", "zigzag", 500000.0)]))
 
     if not args.skip_cpu and ws_list[0].get("cu_seqlens") is None:
         w = ws_list[0]

@@ -27,6 +27,7 @@ ATTN = "attn_bf16_mfma"
 COPY = "copyBuffer"
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["ring_attention_blockwise_ra_amd/csrc/ra_kernels.hip",
+                  "ring_attention_blockwise_ra_amd/csrc/ra_device.h",
                   "ring_attention_blockwise_ra_amd/csrc/ra_sched.h"]
 
 
