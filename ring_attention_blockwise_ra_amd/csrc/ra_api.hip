@@ -444,17 +444,19 @@ struct Stager {
     *v = stage_v[b];
     return RA_OK;
   }
+  // after step `step`'s kernels are enqueued; step 1's block is brought in
+  // once step 0's kernels are queued, so that its copy runs under them
   ra_status done(int step) {
     hipError_t e;
     if (sep && staged(step) && (e = hipEventRecord(de->compute_done[step % 2], cs)) != hipSuccess)
       return hip_fail(e, "hipEventRecord");
+    if (step == 0 && p->n_ring > 1) return stage(1);
     return RA_OK;
   }
-  // the first copies: step 0's block (rotary embedding) and step 1's
+  // the first copy: step 0's block when it is staged (rotary embedding)
   ra_status start() {
     ra_status st = begin();
     if (st == RA_OK && rope) st = stage(0);
-    if (st == RA_OK && p->n_ring > 1) st = stage(1);
     return st;
   }
 };
