@@ -34,6 +34,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ra_device.h"
 #include "ra_kernels.h"
 #include "ra_sched.h"
@@ -322,28 +324,6 @@ struct RowTile {
   static constexpr int SLOT = 2 * TB;            // Q tile then dO tile
 };
 
-// LDS-DMA of one row tile of q (or dO): rows rho0 .. rho0+31 of (segment, KV
-// head), each gathered from its (query index, head) position; rows past the
-// end are clamped to the last row (loaded, never used: their weights are 0).
-template <int D, int NW>
-__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int hq, int hbase, int group,
-                                         int rho0, int rows_total, char* lds_tile, int wave, int lane) {
-  using R = RowTile<D>;
-  constexpr int LPW = (R::SEGS + NW - 1) / NW;
-  const int rin = lane / R::CPR, pc = lane % R::CPR;
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int seg = (wave + j * NW) % R::SEGS;
-    const int row = seg * R::ROWS_PER_SEG + rin;
-    const int lc = pc ^ (swz(row) & (R::CPR - 1));
-    const int rho = min(rho0 + row, rows_total - 1);
-    const int a = rho / group;
-    const int h = hbase + (rho - a * group);
-    __builtin_amdgcn_global_load_lds((const void*)(src + ((int64_t)a * hq + h) * D + lc * 8),
-                                     (lds_void*)(lds_tile + seg * 1024), 16, 0, 0);
-  }
-}
-
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   using T = BfTile<D>;
@@ -433,27 +413,86 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   auto slot_q = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT; };
   auto slot_o = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT + R::TB; };
   auto slot_s = [&](int t) { return stats + (t & (kRowSlots - 1)) * 64; };
+
+  // Row cursors of the DMA: row rho of (segment, KV head) is query index
+  // rho / G, head rho % G. Tiles are issued in order, so each cursor steps by
+  // 32 rows per issue (no division in the loop); rows past the end read the
+  // last row (loaded, never used: their weights are 0).
+  constexpr int LPW_R = (R::SEGS + NW - 1) / NW;
+  const int grp = p.group;
+  const int q32 = kRT / grp, r32 = kRT - q32 * grp;
+  const int last = rows_total - 1, a_last = last / grp, h_last = last - a_last * grp;
+  int c_rho[LPW_R + 1], c_a[LPW_R + 1], c_h[LPW_R + 1];
+  int dma_off[LPW_R], dma_lc[LPW_R];
+  {
+    const int rin = lane / R::CPR, pc = lane % R::CPR;
+#pragma unroll
+    for (int j = 0; j < LPW_R; ++j) {
+      const int seg = (wave + j * NW) % R::SEGS;
+      const int row = seg * R::ROWS_PER_SEG + rin;
+      dma_off[j] = seg * 1024;
+      dma_lc[j] = (pc ^ (swz(row) & (R::CPR - 1))) * 8;
+      c_rho[j] = t_first * kRT + row;
+    }
+    c_rho[LPW_R] = t_first * kRT + col;  // the statistics of row col
+#pragma unroll
+    for (int j = 0; j <= LPW_R; ++j) {
+      c_a[j] = c_rho[j] / grp;
+      c_h[j] = c_rho[j] - c_a[j] * grp;
+    }
+  }
+  auto cursor_off = [&](int j) {  // (query index * hq + head) of cursor j, clamped
+    const bool over = c_rho[j] > last;
+    return (int64_t)(over ? a_last : c_a[j]) * p.hq + hbase + (over ? h_last : c_h[j]);
+  };
+  auto cursor_step = [&](int j) {
+    c_rho[j] += kRT;
+    c_a[j] += q32;
+    c_h[j] += r32;
+    if (c_h[j] >= grp) {
+      c_h[j] -= grp;
+      ++c_a[j];
+    }
+  };
   auto issue = [&](int t) {
-    dma_rows<D, NW>(qg, p.hq, hbase, p.group, t * kRT, rows_total, slot_q(t), wave, lane);
-    dma_rows<D, NW>(og, p.hq, hbase, p.group, t * kRT, rows_total, slot_o(t), wave, lane);
-    // lse (lanes 0-31) and delta (lanes 32-63) of rows 32t + col, clamped
-    const int rc = min(t * kRT + col, rows_total - 1);
-    const int a = rc / p.group;
-    const int64_t sidx = st_off + (int64_t)a * p.hq + hbase + (rc - a * p.group);
+#pragma unroll
+    for (int j = 0; j < LPW_R; ++j) {
+      const int64_t off = cursor_off(j) * D + dma_lc[j];
+      __builtin_amdgcn_global_load_lds((const void*)(qg + off), (lds_void*)(slot_q(t) + dma_off[j]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(og + off), (lds_void*)(slot_o(t) + dma_off[j]), 16, 0, 0);
+      cursor_step(j);
+    }
+    // lse (lanes 0-31) and delta (lanes 32-63) of rows 32t + col
+    const int64_t sidx = st_off + cursor_off(LPW_R);
     const float* src = half == 0 ? p.lse + sidx : p.delta + sidx;
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)slot_s(t), 4, 0, 0);
+    cursor_step(LPW_R);
   };
 
-  // per row tile: does any key of this wave meet a visible row, and do some
-  // of its pairs need the element mask
-  auto active = [&](int t) {
-    const int a_hi = (min(t * kRT + kRT, rows_total) - 1) / p.group;
-    return kw_lo < (int)key_end(geom, a_hi, kv_len);
-  };
-  auto needs_mask = [&](int t) {
-    const int a_lo = (t * kRT) / p.group;
-    return !(kw_lo + 31 < (int)key_end(geom, a_lo, kv_len)) || t * kRT + kRT > rows_total;
-  };
+  // Per row tile: does any key of this wave meet a visible row (from tile
+  // t_act on), and do some of its pairs need the element mask (before tile
+  // t_full, and the ragged last tile). e is nondecreasing, so both are
+  // thresholds, found once by bisection.
+  auto a_hi_of = [&](int t) { return (min(t * kRT + kRT, rows_total) - 1) / grp; };
+  int t_act, t_full;
+  {
+    int lo = t_first, hi = n_rt;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kw_lo < (int)key_end(geom, a_hi_of(mid), kv_len)) hi = mid; else lo = mid + 1;
+    }
+    t_act = lo;
+    lo = t_first;
+    hi = n_rt;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kw_lo + 31 < (int)key_end(geom, (mid * kRT) / grp, kv_len)) hi = mid; else lo = mid + 1;
+    }
+    t_full = lo;
+  }
+  const int t_ragged = (rows_total % kRT) ? n_rt - 1 : n_rt;
+  auto active = [&](int t) { return t >= t_act; };
+  auto needs_mask = [&](int t) { return t < t_full || t >= t_ragged; };
   // S = Q K^T and dP = dO V^T of row tile t (A operands: Q / dO rows in LDS)
   auto scores = [&](int t, f32x16& s, f32x16& dp) {
     const char* sQ = slot_q(t);
@@ -470,14 +509,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
     }
   };
   // P and dS of row tile t as bf16 B operands; element i of this lane is
-  // row 8*(i/4) + 4*half + i%4 of the tile
-  auto weights = [&](int t, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
-    const bool mask = needs_mask(t);
-    if (mask && half == 0) {
+  // row 8*(i/4) + 4*half + i%4 of the tile. The masked form zeroes the
+  // weights of keys at or past each row's limit (rows past the end have
+  // limit 0); tiles before t_act are masked entirely that way.
+  auto weights = [&](auto masked, int t, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2],
+                     bf16x8 (&dsb)[2]) {
+    constexpr bool MASK = decltype(masked)::value;
+    if (MASK && half == 0) {
       const int rho = t * kRT + col;
-      elim[col] = rho < rows_total ? (int)key_end(geom, rho / p.group, kv_len) : 0;
+      elim[col] = rho < rows_total ? (int)key_end(geom, rho / grp, kv_len) : 0;
     }
-    const float* st = slot_s(t);
+    float* st = slot_s(t);
+    {  // lse -> exp2-domain subtrahend, once per row (lanes 0-31 own the lse slots)
+      const float x = st[lane];
+      if (half == 0) st[lane] = lse_to_log2(x);
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       f32x8 p8, d8;
@@ -487,12 +533,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + rbase);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rbase);
         u32x4 e4 = {0u, 0u, 0u, 0u};
-        if (mask) e4 = *reinterpret_cast<const u32x4*>(elim + rbase);
+        if constexpr (MASK) e4 = *reinterpret_cast<const u32x4*>(elim + rbase);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 8 * c + 4 * hq4 + e;
-          float pv = fast_exp2(__builtin_fmaf(s[i], sl2, -lse_to_log2(l4[e])));
-          if (mask && kmy >= (int)e4[e]) pv = 0.f;  // also rows past the end (limit 0)
+          float pv = fast_exp2(__builtin_fmaf(s[i], sl2, -l4[e]));
+          if constexpr (MASK) {
+            if (kmy >= (int)e4[e]) pv = 0.f;
+          }
           p8[4 * hq4 + e] = pv;
           d8[4 * hq4 + e] = pv * (dp[i] - d4[e]);
         }
@@ -522,9 +570,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   // scores, which do not depend on them; then tile t's accumulation.
   auto step = [&](int t, const f32x16& s_cur, const f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt) {
     issue(t + 3);
-    const bool act = active(t);
     bf16x8 pb[2], dsb[2];
-    if (act) weights(t, s_cur, dp_cur, pb, dsb);
+    const bool act = active(t);
+    if (act) {
+      if (needs_mask(t))
+        weights(std::true_type{}, t, s_cur, dp_cur, pb, dsb);
+      else
+        weights(std::false_type{}, t, s_cur, dp_cur, pb, dsb);
+    }
     if (t + 1 < n_rt && active(t + 1)) scores(t + 1, s_nxt, dp_nxt);
     if (act) accumulate(t, pb, dsb);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
