@@ -102,7 +102,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16(BwdParams p) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave values stay scalar
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -324,7 +324,9 @@ struct RowTile {
   static constexpr int SLOT = 2 * TB;            // Q tile then dO tile
 };
 
-template <int D, int NW>
+// REG: the group size divides the row tile (every tile starts at a query
+// index boundary), which lets the row loads use fixed per-lane offsets.
+template <int D, int NW, bool REG>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   using T = BfTile<D>;
   using R = RowTile<D>;
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave limits stay scalar
   const int half = lane >> 5;
   const int col = lane & 31;
   float* stats = reinterpret_cast<float*>(smem + kRowSlots * R::SLOT) + wave * kRowSlots * 64;
@@ -454,18 +456,62 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
       ++c_a[j];
     }
   };
+  // lse (lanes 0-31) or delta (lanes 32-63): the pointer is chosen once and
+  // kept in registers (otherwise the selection between the two parameters
+  // becomes a per-lane load from the parameter block on every tile, with a
+  // wait on all loads in flight)
+  const float* stats_src = half == 0 ? p.lse : p.delta;
+  asm volatile("" : "+v"(stats_src));
+  // REG: tile t holds query indices [t*qpt, (t+1)*qpt) and each lane's row
+  // sits at a fixed byte offset from the tile's first row (ro); in the last
+  // tile rows past the end re-read its last valid row (ro_last).
+  const int qpt = kRT / grp;
+  const int vr = rows_total - (n_rt - 1) * kRT;  // valid rows of the last tile
+  uint32_t ro[LPW_R + 1], ro_last[LPW_R + 1];
+  if constexpr (REG) {
+    const int rin = lane / R::CPR;
+#pragma unroll
+    for (int j = 0; j <= LPW_R; ++j) {
+      // Q / dO rows (j < LPW_R): bytes of the (query, head) row plus the
+      // lane's chunk; the statistics (j = LPW_R): 4 bytes per (query, head)
+      const int row = j < LPW_R ? ((wave + j * NW) % R::SEGS) * R::ROWS_PER_SEG + rin : col;
+      const int rl = min(row, vr - 1);
+      const int qh = (row / grp) * p.hq + hbase + row % grp;
+      const int qhl = (rl / grp) * p.hq + hbase + rl % grp;
+      if (j < LPW_R) {
+        ro[j] = (uint32_t)(qh * D + dma_lc[j]) * 2u;
+        ro_last[j] = (uint32_t)(qhl * D + dma_lc[j]) * 2u;
+      } else {
+        ro[j] = (uint32_t)qh * 4u;
+        ro_last[j] = (uint32_t)qhl * 4u;
+      }
+    }
+  }
   auto issue = [&](int t) {
+    if constexpr (REG) {
+      const int te = min(t, n_rt - 1);
+      const bool lt = te == n_rt - 1;
+      const int64_t tq = (int64_t)te * qpt * p.hq;  // first (query, head) index of the tile
+#pragma unroll
+      for (int j = 0; j < LPW_R; ++j) {
+        const uint32_t off = lt ? ro_last[j] : ro[j];
+        lds_dma_off<16>(qg + tq * D, off, slot_q(t) + dma_off[j]);
+        lds_dma_off<16>(og + tq * D, off, slot_o(t) + dma_off[j]);
+      }
+      const char* src = reinterpret_cast<const char*>(stats_src + st_off + tq);
+      lds_dma<4>(src + (lt ? ro_last[LPW_R] : ro[LPW_R]), reinterpret_cast<char*>(slot_s(t)));
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < LPW_R; ++j) {
       const int64_t off = cursor_off(j) * D + dma_lc[j];
-      __builtin_amdgcn_global_load_lds((const void*)(qg + off), (lds_void*)(slot_q(t) + dma_off[j]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(og + off), (lds_void*)(slot_o(t) + dma_off[j]), 16, 0, 0);
+      lds_dma<16>((const void*)(qg + off), slot_q(t) + dma_off[j]);
+      lds_dma<16>((const void*)(og + off), slot_o(t) + dma_off[j]);
       cursor_step(j);
     }
     // lse (lanes 0-31) and delta (lanes 32-63) of rows 32t + col
-    const int64_t sidx = st_off + cursor_off(LPW_R);
-    const float* src = half == 0 ? p.lse + sidx : p.delta + sidx;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)slot_s(t), 4, 0, 0);
+    const float* src = stats_src + st_off + cursor_off(LPW_R);
+    lds_dma<4>((const void*)src, reinterpret_cast<char*>(slot_s(t)));
     cursor_step(LPW_R);
   };
 
@@ -522,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
     float* st = slot_s(t);
     {  // lse -> exp2-domain subtrahend, once per row (lanes 0-31 own the lse slots)
       const float x = st[lane];
-      if (half == 0) st[lane] = lse_to_log2(x);
+      st[lane] = half == 0 ? lse_to_log2(x) : x;  // a select keeps the step one block
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -596,7 +642,42 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
     f32x16 sA, dA, sB, dB;
     if (active(t_first)) scores(t_first, sA, dA);
+    // Three phases: masked tiles before t_full, then the steady state (tile
+    // t active and unmasked, a next tile exists) as one branch-free block per
+    // step, so the scores of t+1 interleave with the weights of t; then the
+    // ragged last tile. After an odd number of steps the score registers
+    // swap roles once.
+    auto fast_step = [&](int tt, const f32x16& s_cur, const f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt) {
+      issue(tt + 3);
+      bf16x8 pb[2], dsb[2];
+      weights(std::false_type{}, tt, s_cur, dp_cur, pb, dsb);
+      scores(tt + 1, s_nxt, dp_nxt);
+      accumulate(tt, pb, dsb);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
+    };
+    const int e1 = max(t_first, min(t_full, n_rt));
+    const int e2 = max(e1, min(n_rt - 1, t_ragged));
     int t = t_first;
+    for (; t + 1 < e1; t += 2) {
+      step(t, sA, dA, sB, dB);
+      step(t + 1, sB, dB, sA, dA);
+    }
+    if (t < e1) {
+      step(t, sA, dA, sB, dB);
+      sA = sB;
+      dA = dB;
+      ++t;
+    }
+    for (; t + 1 < e2; t += 2) {
+      fast_step(t, sA, dA, sB, dB);
+      fast_step(t + 1, sB, dB, sA, dA);
+    }
+    if (t < e2) {
+      fast_step(t, sA, dA, sB, dB);
+      sA = sB;
+      dA = dB;
+      ++t;
+    }
     for (; t + 1 < n_rt; t += 2) {
       step(t, sA, dA, sB, dB);
       step(t + 1, sB, dB, sA, dA);
@@ -842,13 +923,14 @@ static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
     BwdParams q = p;
     const int64_t tiles = set_tiles_bwd(q, 32 * kKvWaves, true);
     const size_t smem = kRowSlots * RowTile<D>::SLOT + kKvWaves * (kRowSlots * 64 + 32) * 4;
-    auto kern = bwd_dkdv_bf16<D, kKvWaves>;
-    static bool attr_set = false;
-    if (!attr_set) {
+    const bool reg = kRT % q.group == 0;
+    auto kern = reg ? bwd_dkdv_bf16<D, kKvWaves, true> : bwd_dkdv_bf16<D, kKvWaves, false>;
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[reg]) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
       if (e != hipSuccess) return e;
-      attr_set = true;
+      attr_set[reg] = true;
     }
     const int64_t grid = (int64_t)q.batch * q.hkv * tiles;
     if (grid > 0) hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kKvWaves * 64), smem, stream, q);

@@ -109,6 +109,43 @@ __device__ __forceinline__ TileRef locate_tile(const Params& p) {
   return t;
 }
 
+// One direct global -> LDS load (global_load_lds_dword / _dwordx4): lane l
+// reads BYTES bytes at its own global address and writes them to
+// dst + BYTES*l; dst is wave-uniform and goes to M0. Issued from inline
+// assembly rather than through the compiler builtin: for the builtin the
+// compiler also waits for every LDS load in flight (vmcnt(0)) before each
+// transposed LDS read (ds_read_b64_tr_b16), which would drain the tiles the
+// rings keep in flight on every step. The kernels order these loads
+// themselves (s_waitcnt vmcnt(n) + s_barrier before a tile is read, and a
+// slot is refilled only after the barrier that ends its last read). The
+// s_nop covers the one wait state required between writing M0 and an LDS
+// load that uses it.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* src, char* dst) {
+  static_assert(BYTES == 4 || BYTES == 16, "global_load_lds moves 4 or 16 bytes per lane");
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)dst);
+  if constexpr (BYTES == 16)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// The same with a wave-uniform base address (forced into scalar registers)
+// and a 32-bit per-lane byte offset from it.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma_off(const void* base, uint32_t off, char* dst) {
+  static_assert(BYTES == 4 || BYTES == 16, "global_load_lds moves 4 or 16 bytes per lane");
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)dst);
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b64 >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+  const void* sbase = (const void*)(uintptr_t)sb;
+  if constexpr (BYTES == 16)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "{m0}"(m0) : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Direct global -> LDS copy of one K or V tile (global_load_lds_dwordx4: lane
 // l of an instruction writes bytes [16l, 16l+16) of a 1 KiB LDS segment and
 // reads any global address). Every wave issues LPW instructions, so the
@@ -126,8 +163,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int r
     const int row = seg * T::ROWS_PER_SEG + rin;
     const int lc = pc ^ (swz(row) & (T::CPR - 1));
     const int key = min(key0 + row, kv_len - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + key * row_stride + lc * 8),
-                                     (lds_void*)(lds_tile + seg * 1024), 16, 0, 0);
+    lds_dma<16>((const void*)(src + key * row_stride + lc * 8), lds_tile + seg * 1024);
   }
 }
 

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave values stay scalar
   const int half = lane >> 5;
   const int col = lane & 31;
 

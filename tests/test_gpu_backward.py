@@ -81,6 +81,8 @@ def test_delta_kernel():
     (torch.bfloat16, 64, 2, 2, 97, 2, "contiguous", False),
     (torch.bfloat16, 32, 3, 1, 70, 4, "striped", True),
     (torch.bfloat16, 16, 2, 2, 66, 3, "zigzag", True),
+    (torch.bfloat16, 128, 6, 1, 150, 2, "contiguous", False),
+    (torch.bfloat16, 64, 8, 1, 120, 2, "striped", True),
     (torch.float32, 128, 4, 2, 90, 3, "contiguous", True),
     (torch.float32, 64, 2, 1, 64, 2, "zigzag", True),
     (torch.float32, 16, 1, 1, 33, 3, "striped", False),
