@@ -907,16 +907,11 @@ static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
     const int64_t tiles = set_tiles_bwd(q, 32 * kDqWaves, false);
     const size_t smem = kSlots * BfTile<D>::SLOT;
     auto kern = bwd_dq_bf16<D, kDqWaves>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
+    if (e != hipSuccess) return e;
     const int64_t grid = (int64_t)q.batch * q.hkv * tiles;
     if (grid > 0) hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDqWaves * 64), smem, stream, q);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
@@ -925,13 +920,8 @@ static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
     const size_t smem = kRowSlots * RowTile<D>::SLOT + kKvWaves * (kRowSlots * 64 + 32) * 4;
     const bool reg = kRT % q.group == 0;
     auto kern = reg ? bwd_dkdv_bf16<D, kKvWaves, true> : bwd_dkdv_bf16<D, kKvWaves, false>;
-    static bool attr_set[2] = {false, false};
-    if (!attr_set[reg]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      if (e != hipSuccess) return e;
-      attr_set[reg] = true;
-    }
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
+    if (e != hipSuccess) return e;
     const int64_t grid = (int64_t)q.batch * q.hkv * tiles;
     if (grid > 0) hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kKvWaves * 64), smem, stream, q);
   }

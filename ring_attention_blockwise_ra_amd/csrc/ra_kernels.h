@@ -96,6 +96,10 @@ struct RopeParams {
 };
 hipError_t launch_rope(const RopeParams& p, hipStream_t stream);
 
+// Raises the dynamic LDS limit of `kern` to `bytes` on the current device
+// (once per kernel and device).
+hipError_t allow_dynamic_lds(const void* kern, size_t bytes);
+
 // waves: wavefronts per workgroup of the bf16 kernel (4 or 8; 32 rows each).
 hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream);
 

@@ -27,6 +27,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "ra_device.h"
 #include "ra_kernels.h"
 #include "ra_sched.h"
@@ -531,19 +535,29 @@ static int64_t set_tiles(AttnParams& p, int rows_per_tile) {
   return total;
 }
 
+// Kernels that use more than 64 KiB of dynamic LDS need the limit raised once
+// per (kernel, device); the pairs already done are remembered.
+hipError_t allow_dynamic_lds(const void* kern, size_t bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kern, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.insert({kern, dev});
+  return e;
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
   constexpr int ROWS = 32 * NW;
   const int64_t tiles = set_tiles(p, ROWS);
   const size_t smem = kSlots * BfTile<D>::SLOT;  // ring of K/V tile slots
   auto kern = attn_bf16_mfma<D, NW>;
-  static bool attr_set = false;  // per instantiation; benign race (idempotent)
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
+  if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)p.batch * p.hkv * tiles;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), smem, stream, p);
