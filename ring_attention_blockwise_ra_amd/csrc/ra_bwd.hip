@@ -95,8 +95,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16(BwdParams p) {
   using T = BfTile<D>;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = T::DP / 32;
-  constexpr int LPW = (T::SEGS + NW - 1) / NW;
-  constexpr int LOADS_PER_TILE = 2 * LPW;
+  constexpr int LOADS_PER_TILE = 2 * KvTileDma<D, NW>::LPW;  // per wave: K and V
   constexpr int ROWS = 32 * NW;
 
   extern __shared__ __align__(16) char smem[];
@@ -180,9 +179,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16(BwdParams p) {
 
   auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT; };
   auto slot_v = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT + T::TB; };
+  const KvTileDma<D, NW> kv_dma(kv_len, kv_row_stride, wave, lane);
   auto issue = [&](int t) {
-    dma_tile<D, NW>(kg, kv_row_stride, t * kTK, kv_len, slot_k(t), wave, lane);
-    dma_tile<D, NW>(vg, kv_row_stride, t * kTK, kv_len, slot_v(t), wave, lane);
+    kv_dma.issue(kg, t, slot_k(t));
+    kv_dma.issue(vg, t, slot_v(t));
   };
   // 32 keys: unit u is half u%2 of tile u/2
   auto unit = [&](int u) {
@@ -416,10 +416,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   auto slot_o = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT + R::TB; };
   auto slot_s = [&](int t) { return stats + (t & (kRowSlots - 1)) * 64; };
 
-  // Row cursors of the DMA: row rho of (segment, KV head) is query index
-  // rho / G, head rho % G. Tiles are issued in order, so each cursor steps by
-  // 32 rows per issue (no division in the loop); rows past the end read the
-  // last row (loaded, never used: their weights are 0).
+  // Row cursors of the DMA (groups that do not divide the row tile): row rho
+  // of (segment, KV head) is query index rho / G, head rho % G. Tiles are
+  // issued in order, so each cursor steps by 32 rows per issue (no division
+  // in the loop); rows past the end read the last row (loaded, never used:
+  // their weights are 0). dma_off / dma_lc (the LDS segment and swizzled
+  // chunk of each lane) serve both forms.
   constexpr int LPW_R = (R::SEGS + NW - 1) / NW;
   const int grp = p.group;
   const int q32 = kRT / grp, r32 = kRT - q32 * grp;

@@ -146,26 +146,47 @@ __device__ __forceinline__ void lds_dma_off(const void* base, uint32_t off, char
     asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
-// Direct global -> LDS copy of one K or V tile (global_load_lds_dwordx4: lane
-// l of an instruction writes bytes [16l, 16l+16) of a 1 KiB LDS segment and
-// reads any global address). Every wave issues LPW instructions, so the
-// per-wave count of outstanding loads is the same in all waves. Key rows past
-// kv_len re-read the last row; those keys are masked before the softmax.
+// Copies of K or V tiles (kTK keys x D) global -> LDS by global_load_lds_dwordx4
+// (lane l of an instruction writes bytes [16l, 16l+16) of a 1 KiB LDS segment
+// and reads any global address). A lane's row and chunk within a tile are
+// fixed, so its byte offset from the tile's first key is too, and the tile
+// base is a scalar. Key rows past kv_len re-read the last key (those keys are
+// masked before the softmax); tiles past the last one that holds keys reload
+// it (they are never read). Every wave issues LPW instructions per tile, so
+// all waves have the same count of loads in flight. kv_len >= 1.
 template <int D, int NW>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int row_stride, int key0,
-                                         int kv_len, char* lds_tile, int wave, int lane) {
+struct KvTileDma {
   using T = BfTile<D>;
-  constexpr int LPW = T::SEGS >= NW ? T::SEGS / NW : 1;
-  const int rin = lane / T::CPR, pc = lane % T::CPR;
+  static constexpr int LPW = T::SEGS >= NW ? T::SEGS / NW : 1;
+  uint32_t off[LPW], off_last[LPW];  // bytes from the tile base
+  int seg[LPW];                       // LDS byte offset of the lane's segment
+  int n_real;                         // tiles holding keys
+  int64_t tile_elems;                 // elements from one tile base to the next
+
+  __device__ __forceinline__ KvTileDma(int kv_len, int row_stride, int wave, int lane) {
+    n_real = (kv_len + kTK - 1) / kTK;
+    tile_elems = (int64_t)kTK * row_stride;
+    const int last_row = kv_len - (n_real - 1) * kTK - 1;  // in the last real tile
+    const int rin = lane / T::CPR, pc = lane % T::CPR;
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int seg = (wave + j * NW) % T::SEGS;
-    const int row = seg * T::ROWS_PER_SEG + rin;
-    const int lc = pc ^ (swz(row) & (T::CPR - 1));
-    const int key = min(key0 + row, kv_len - 1);
-    lds_dma<16>((const void*)(src + key * row_stride + lc * 8), lds_tile + seg * 1024);
+    for (int j = 0; j < LPW; ++j) {
+      const int sg = (wave + j * NW) % T::SEGS;
+      const int row = sg * T::ROWS_PER_SEG + rin;
+      const int lc = pc ^ (swz(row) & (T::CPR - 1));
+      seg[j] = sg * 1024;
+      off[j] = (uint32_t)(row * row_stride + lc * 8) * 2u;
+      off_last[j] = (uint32_t)(min(row, last_row) * row_stride + lc * 8) * 2u;
+    }
   }
-}
+  // tile t of src into the LDS tile at dst
+  __device__ __forceinline__ void issue(const uint16_t* src, int t, char* dst) const {
+    const int te = min(t, n_real - 1);
+    const bool last = te == n_real - 1;
+    const uint16_t* base = src + te * tile_elems;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) lds_dma_off<16>(base, last ? off_last[j] : off[j], dst + seg[j]);
+  }
+};
 
 
 }  // namespace ra

@@ -76,8 +76,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   constexpr int KB = kTK / 32;   // 32-key blocks per tile
   constexpr int KC = kTK / 16;   // 16-key chunks per tile
   constexpr int DB = T::DP / 32; // 32-dim blocks of the output
-  constexpr int LPW = T::SEGS >= NW ? T::SEGS / NW : 1;
-  constexpr int LOADS_PER_TILE = 2 * LPW;  // per wave: K and V
+  constexpr int LOADS_PER_TILE = 2 * KvTileDma<D, NW>::LPW;  // per wave: K and V
 
   extern __shared__ __align__(16) char smem[];
 
@@ -171,9 +170,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
 
   auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT; };
   auto slot_v = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT + T::TB; };
+  const KvTileDma<D, NW> kv_dma(kv_len, kv_row_stride, wave, lane);
   auto issue = [&](int t) {
-    dma_tile<D, NW>(kg, kv_row_stride, t * kTK, kv_len, slot_k(t), wave, lane);
-    dma_tile<D, NW>(vg, kv_row_stride, t * kTK, kv_len, slot_v(t), wave, lane);
+    kv_dma.issue(kg, t, slot_k(t));
+    kv_dma.issue(vg, t, slot_v(t));
   };
   // Work is done in units of 32 keys: unit u is half u%2 of tile u/2. S(u)
   // is one 32x32 MFMA tile (16 registers per lane), P(u) two bf16x8 operands.
