@@ -331,8 +331,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the ring; runs on more than one GPU are "
-              "not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's share of the ring; multi-GPU runs are not "
+              "supported (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
