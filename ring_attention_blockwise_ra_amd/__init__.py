@@ -9,7 +9,8 @@ its absence is an error, never a fallback.
 _BINDING_NAMES = (
     "ra_block_attn_partial", "ra_merge_partials", "ra_finalize", "ra_ring_workspace_bytes",
     "ra_ring_fwd", "ra_tile_class_host", "ra_tile_classes_host", "ra_tile_classes_device",
-    "make_problem", "RaError", "RaProblem", "lib",
+    "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
+    "ra_rope_apply", "make_problem", "RaError", "RaProblem", "lib",
 )
 
 __all__ = list(_BINDING_NAMES)
