@@ -977,7 +977,7 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(int64_t n4, f32x4* x) {
 hipError_t launch_zero(float* x, int64_t n, hipStream_t stream) {
   const int64_t n4 = n / 4;  // callers pass multiples of 4 (rows * head_dim)
   int64_t blocks = (n4 + kThreads - 1) / kThreads;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, n4,
                      reinterpret_cast<f32x4*>(x));
@@ -988,7 +988,7 @@ hipError_t launch_bwd_delta(int64_t rows, int d, int is_bf16, const float* out, 
                             float* delta, hipStream_t stream) {
   const int vpr = d / 4;
   int64_t blocks = (rows * vpr + kThreads - 1) / kThreads;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, rows, vpr,
                      reinterpret_cast<const f32x4*>(out), dout, is_bf16, delta);

@@ -30,6 +30,11 @@ constexpr float kRescale = 8.0f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr int kThreads = 256;  // workgroup size of the fp32 and elementwise kernels
+// The elementwise kernels (merge, finalize, fills, delta, rotation) loop
+// grid-stride but are launched with one workgroup per kThreads work items up
+// to this many: a grid covering the whole array keeps far more loads in
+// flight than a smaller grid looping over it (merge 4.5 -> 5.9 TB/s).
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 24;
 constexpr int kTK = 64;        // keys per tile
 constexpr int kSlots = 4;      // LDS ring of K/V tiles; loads run kSlots-1 tiles ahead
 

@@ -517,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void tile_classes_kernel(int kind, int de
 // ---------------------------------------------------------------------------
 static int grid_for(int64_t total_threads) {
   int64_t blocks = (total_threads + kThreads - 1) / kThreads;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
   if (blocks < 1) blocks = 1;
   return (int)blocks;
 }

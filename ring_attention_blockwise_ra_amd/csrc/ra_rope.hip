@@ -94,7 +94,7 @@ hipError_t launch_rope(const RopeParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.batch * p.len * p.heads * (p.head_dim / 8);
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 16384) blocks = 16384;
+  if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
   hipLaunchKernelGGL(rope_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
