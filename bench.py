@@ -54,6 +54,71 @@ def timed(fn, stream=None):
     return e0.elapsed_time(e1)
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clock and socket power (amdsmi GPU metrics)
+    on a background thread while a timed region runs. The firmware refreshes
+    these metrics about once a second. Every failure (no amdsmi, no access to
+    the metrics) leaves the result None; timing never depends on it."""
+
+    MAX_GFXCLK_MHZ = 2400.0   # MI355X peak engine clock, the clock of the published peaks
+
+    def __init__(self, period_s=0.05):
+        self.period_s = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        self._smi = None
+        self._h = None
+        self.power_cap_w = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) == 1:   # the one GPU this process uses
+                self._smi, self._h = amdsmi, hs[0]
+                cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
+                self.power_cap_w = cap / 1e6 if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception:
+            self._smi = None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                clk, pw = m.get("current_gfxclk"), m.get("current_socket_power")
+                if isinstance(clk, (int, float)) and isinstance(pw, (int, float)):
+                    self.samples.append((float(clk), float(pw)))
+            except Exception:
+                pass
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self._smi is not None:
+            import threading
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        clks = sorted(c for c, _ in self.samples)
+        pws = sorted(p for _, p in self.samples)
+        med = lambda xs: xs[len(xs) // 2]
+        return {"gfxclk_mhz_median": med(clks), "gfxclk_mhz_min": clks[0], "gfxclk_mhz_max": clks[-1],
+                "gfxclk_mhz_peak_spec": self.MAX_GFXCLK_MHZ,
+                "socket_power_w_median": med(pws), "power_cap_w": self.power_cap_w,
+                "samples": len(self.samples),
+                "source": "amdsmi GPU metrics sampled during the timed steps (firmware refresh ~1 s)"}
+
+
 def ring_call(w, out, lse, ws, copy_stream="auto"):
     c = w["cfg"]
     return B.ra_ring_fwd(w["q"], w["k"], w["v"], n_ring=c["n_ring"], causal=c["causal"],
@@ -400,13 +465,16 @@ def main():
 
     torch.cuda.synchronize()
     per_layout_ms = {w["layout"]: 0.0 for w in ws_list}
+    sampler = ClockSampler()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        for w in ws_list:
-            per_layout_ms[w["layout"]] += timed(lambda: ring_call(w, w["out"], w["lse"], w["ws"]))
-        log(f"[bench] step {i + 1}/{args.steps} done")
-    torch.cuda.synchronize()
+    with sampler:
+        for i in range(args.steps):
+            for w in ws_list:
+                per_layout_ms[w["layout"]] += timed(lambda: ring_call(w, w["out"], w["lse"], w["ws"]))
+            log(f"[bench] step {i + 1}/{args.steps} done")
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    clock = sampler.summary()
     total_ms = sum(per_layout_ms.values())
     ms_per_step = total_ms / args.steps
     total_flops = sum(w["flops"] for w in ws_list) * args.steps
@@ -436,6 +504,7 @@ def main():
         },
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 2),
+        "clock": clock,
         "layouts": {
             w["layout"]: {"ms": round(per_layout_ms[w["layout"]] / args.steps, 3),
                           "tflops": round(w["flops"] / (per_layout_ms[w["layout"]] / args.steps / 1e3) / 1e12, 2),
@@ -464,6 +533,11 @@ def main():
             "flops_per_launch_avg": kf / max(nl, 1),
             "kernel_source_hash": src_hash,
         }
+        if clock:
+            # the same peak scaled to the engine clock observed in the timed steps
+            peak_obs = PEAK_BF16_TFLOPS * clock["gfxclk_mhz_median"] / ClockSampler.MAX_GFXCLK_MHZ
+            result["roofline"]["peak_at_observed_clock"] = round(peak_obs, 1)
+            result["roofline"]["frac_at_observed_clock"] = round(achieved / peak_obs, 4)
         log("[bench] kernel leg done")
         # every layout, so that the attention launches of the whole run have the
         # same mix as the kernel leg (its average is compared with rocprofv3's)
