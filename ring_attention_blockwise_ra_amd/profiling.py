@@ -2,6 +2,7 @@
 
     python -m ring_attention_blockwise_ra_amd.profiling trace  <kernel_trace.csv> <kernel_stats.csv>
     python -m ring_attention_blockwise_ra_amd.profiling traffic <fetch_dir> <write_dir> <out.json>
+    python -m ring_attention_blockwise_ra_amd.profiling sq <pmc_dir>
 
 trace:   per-kernel statistics of the attention, merge and finalize kernels,
          and how much of the side-queue staging copy time ran while an
@@ -11,6 +12,12 @@ traffic: HBM bytes per attention launch from two counter runs (FETCH_SIZE,
          counter reads for the calibration copy of known size that bench.py
          performs with --calib-copy-mib. Writes a JSON that bench.py reports
          as roofline.traffic while the kernel source hash still matches.
+sq:      shader-sequencer counters of the attention launches (one --pmc run
+         with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU,
+         SQ_INSTS_VALU_TRANS_F32, SQ_INSTS_LDS, GRBM_GUI_ACTIVE and others):
+         matrix-core busy fraction per SIMD cycle, the engine clock implied by
+         GRBM_GUI_ACTIVE over the dispatch times, executed MFMA FLOPs and
+         instruction mix per MFMA.
 """
 
 from __future__ import annotations
@@ -109,6 +116,51 @@ def traffic(fetch_dir: str, write_dir: str, calib_bytes: int) -> dict:
     return res
 
 
+MFMA_FLOPS = 32 * 32 * 16 * 2   # one v_mfma_f32_32x32x16_bf16
+
+
+def sq_summary(run_dir: str, kernel: str = ATTN) -> dict:
+    """Counters summed over the dispatches of `kernel`. GRBM_GUI_ACTIVE sums
+    the busy cycles of every XCD, so per-XCD cycles are that over Num_Xcc;
+    SQ_VALU_MFMA_BUSY_CYCLES sums matrix-core busy cycles over all SIMDs."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {run_dir}")
+    sums = defaultdict(float)
+    spans = {}
+    for path in files:
+        for r in _rows(path):
+            if kernel not in r.get("Kernel_Name", ""):
+                continue
+            sums[r["Counter_Name"]] += float(r["Counter_Value"])
+            did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            spans[did] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    agents = glob.glob(os.path.join(run_dir, "**", "*agent_info.csv"), recursive=True)
+    simds = n_xcc = None
+    for path in agents:
+        for r in _rows(path):
+            if r.get("Name", "").startswith("gfx"):
+                simds, n_xcc = int(r["Simd_Count"]), int(r["Num_Xcc"])
+    dur_ns = sum(e - s for s, e in spans.values())
+    out = dict(kernel=kernel, dispatches=len(spans), duration_ms=dur_ns / 1e6,
+               counters={k: v for k, v in sorted(sums.items())}, simd_count=simds, num_xcc=n_xcc)
+    grbm = sums.get("GRBM_GUI_ACTIVE")
+    if grbm and n_xcc and dur_ns:
+        cyc = grbm / n_xcc
+        out["engine_clock_ghz"] = cyc / dur_ns
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in sums and simds:
+            out["mfma_busy_frac"] = sums["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
+    n_mfma = sums.get("SQ_INSTS_MFMA")
+    if n_mfma:
+        out["mfma_executed_flops"] = n_mfma * MFMA_FLOPS
+        if dur_ns:
+            out["mfma_executed_tflops"] = n_mfma * MFMA_FLOPS / dur_ns / 1e3
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
+            if k in sums:
+                out[k.lower() + "_per_mfma"] = sums[k] / n_mfma
+    return out
+
+
 def main(argv):
     if len(argv) >= 3 and argv[0] == "trace":
         print(json.dumps(trace_summary(argv[1], argv[2]), indent=1))
@@ -119,6 +171,8 @@ def main(argv):
         with open(argv[3], "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t, indent=1))
+    elif len(argv) >= 2 and argv[0] == "sq":
+        print(json.dumps(sq_summary(argv[1]), indent=1))
     else:
         print(__doc__)
         return 2
