@@ -1,0 +1,85 @@
+"""Host-side summaries of rocprofv3 output (profiling.py) on small synthetic CSVs."""
+
+import csv
+import os
+
+import pytest
+
+from ring_attention_blockwise_ra_amd import profiling as P
+
+
+def _write(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0].keys()))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_trace_summary_counts_copy_time_under_attention(tmp_path):
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    rows = [
+        dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=100, End_Timestamp=200),
+        dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=300, End_Timestamp=400),
+        # side-queue copies: fully under the first launch, half under the second, outside
+        dict(Kernel_Name="__amd_rocclr_copyBuffer", Queue_Id=2, Start_Timestamp=120, End_Timestamp=160),
+        dict(Kernel_Name="__amd_rocclr_copyBuffer", Queue_Id=2, Start_Timestamp=380, End_Timestamp=420),
+        dict(Kernel_Name="__amd_rocclr_copyBuffer", Queue_Id=2, Start_Timestamp=500, End_Timestamp=510),
+        # a copy on the attention queue is not a staging copy
+        dict(Kernel_Name="__amd_rocclr_copyBuffer", Queue_Id=1, Start_Timestamp=210, End_Timestamp=290),
+    ]
+    _write(str(tmp_path / "t.csv"), rows)
+    _write(str(tmp_path / "s.csv"), [dict(Name=attn, Calls=2, AverageNs=100.0, TotalDurationNs=200.0,
+                                          Percentage=50.0)])
+    s = P.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "s.csv"))
+    assert s["staging_copies"] == 3
+    assert s["staging_copy_ms"] == pytest.approx(90e-6)
+    assert s["staging_copy_hidden_ms"] == pytest.approx(60e-6)
+    assert s["staging_copy_hidden_frac"] == pytest.approx(60 / 90)
+    (st,) = s["kernels"].values()
+    assert st["calls"] == 2 and st["avg_ms"] == pytest.approx(1e-4)
+
+
+def test_traffic_scales_by_calibration_copy(tmp_path):
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    for counter, d, calib_kib, per in (("FETCH_SIZE", "f", 2 * 1024 * 1024, [300.0, 500.0]),
+                                       ("WRITE_SIZE", "w", 1024 * 1024, [100.0, 100.0])):
+        rows = [dict(Dispatch_Id=1, Kernel_Name="__amd_rocclr_copyBuffer", Counter_Name=counter,
+                     Counter_Value=calib_kib),
+                dict(Dispatch_Id=2, Kernel_Name="__amd_rocclr_copyBuffer", Counter_Name=counter,
+                     Counter_Value=10.0)]
+        # the second attention dispatch reports two instances that are summed
+        rows += [dict(Dispatch_Id=3, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[0]),
+                 dict(Dispatch_Id=4, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[1] / 2),
+                 dict(Dispatch_Id=4, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[1] / 2)]
+        _write(str(tmp_path / d / "x_counter_collection.csv"), rows)
+    t = P.traffic(str(tmp_path / "f"), str(tmp_path / "w"), 1 << 30)
+    # FETCH reads 2 GiB for the 1 GiB copy: factor 1/2
+    assert t["FETCH_SIZE"]["factor"] == pytest.approx(0.5)
+    assert t["FETCH_SIZE"]["bytes_per_launch"] == pytest.approx(400.0 * 1024 * 0.5)
+    assert t["WRITE_SIZE"]["bytes_per_launch"] == pytest.approx(100.0 * 1024)
+    assert t["hbm_bytes_per_launch"] == pytest.approx(400.0 * 512 + 100.0 * 1024)
+
+
+def test_sq_summary_busy_fraction_and_clock(tmp_path):
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    # two dispatches of 1 ms each; 8 XCDs at 2 GHz -> 2e6 cycles per XCD each
+    rows = []
+    for did, (s, e) in ((1, (0, 1_000_000)), (2, (2_000_000, 3_000_000))):
+        for name, val in (("GRBM_GUI_ACTIVE", 8 * 2e6), ("SQ_INSTS_MFMA", 1000.0),
+                          ("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 2e6 * 1024), ("SQ_INSTS_VALU", 6000.0),
+                          ("SQ_INSTS_LDS", 1500.0)):
+            rows.append(dict(Dispatch_Id=did, Kernel_Name=attn, Counter_Name=name, Counter_Value=val,
+                             Start_Timestamp=s, End_Timestamp=e))
+    rows.append(dict(Dispatch_Id=3, Kernel_Name="other", Counter_Name="SQ_INSTS_MFMA", Counter_Value=9e9,
+                     Start_Timestamp=0, End_Timestamp=1))
+    _write(str(tmp_path / "r" / "x_counter_collection.csv"), rows)
+    _write(str(tmp_path / "r" / "x_agent_info.csv"),
+           [dict(Name="cpu", Simd_Count=0, Num_Xcc=0), dict(Name="gfx950", Simd_Count=1024, Num_Xcc=8)])
+    s = P.sq_summary(str(tmp_path / "r"))
+    assert s["dispatches"] == 2
+    assert s["engine_clock_ghz"] == pytest.approx(2.0)
+    assert s["mfma_busy_frac"] == pytest.approx(0.5)
+    assert s["mfma_executed_flops"] == 2000 * 32 * 32 * 16 * 2
+    assert s["sq_insts_valu_per_mfma"] == pytest.approx(6.0)
+    assert s["sq_insts_lds_per_mfma"] == pytest.approx(1.5)
