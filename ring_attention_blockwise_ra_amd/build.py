@@ -3,7 +3,9 @@
     python -m ring_attention_blockwise_ra_amd.build
 
 compiles csrc/*.hip with hipcc (one object per source, in parallel) and links
-ring_attention_blockwise_ra_amd/_lib/libra_amd.so. Every call recompiles.
+ring_attention_blockwise_ra_amd/_lib/libra_amd.so, then the plain-C client
+_lib/ra_capi_ring (tests/capi_ring.c) that the GPU tests run. Every call
+recompiles.
 """
 
 from __future__ import annotations
@@ -61,7 +63,27 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    build_c_client()
     return LIB
+
+
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "capi_ring.c")
+C_CLIENT = os.path.join(LIBDIR, "ra_capi_ring")
+
+
+def build_c_client() -> str | None:
+    """The plain-C ring client the GPU tests run (tests/capi_ring.c): C99,
+    the HIP runtime's C API and libra_amd.so only, found beside it."""
+    if not os.path.exists(C_CLIENT_SRC):
+        return None
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    tmp = C_CLIENT + ".tmp"
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(rocm, "include"), "-I", INCLUDE, C_CLIENT_SRC,
+          "-L", LIBDIR, "-lra_amd", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp])
+    os.replace(tmp, C_CLIENT)
+    return C_CLIENT
 
 
 if __name__ == "__main__":
