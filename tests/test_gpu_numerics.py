@@ -151,3 +151,80 @@ def test_ring_large_magnitude_scores(dtype, layout):
     tol, tol_lse = _f32_bounds(q, k, v) if dtype == "f32" else (TOL[torch.bfloat16], LSE_TOL["bf16"])
     assert err <= tol, (err, tol)
     assert err_lse <= tol_lse, (err_lse, tol_lse)
+
+
+def _term_scales(q, k, v, dout, causal):
+    """Magnitude of the summed terms of each gradient, |dS| |k| scale for dq,
+    |dS|^T |q| scale for dk, P^T |dout| for dv (fp64, plain softmax): under a
+    score ramp dS sums to zero against keys that share a large component, so
+    the gradients are small differences of large terms, and rounding P and dS
+    to bfloat16 (2^-9 each) errs relative to the terms, not to the result."""
+    q, k, v, dout = (_np64(t)[0] for t in (q, k, v, dout))
+    seq, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    vis = np.tril(np.ones((seq, seq), dtype=bool)) if causal else np.ones((seq, seq), dtype=bool)
+    tq, tk, tv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for h in range(hq):
+        g = h * hkv // hq
+        s_ = np.where(vis, q[:, h] @ k[:, g].T * scale, -np.inf)
+        p = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ v[:, g]
+        ds = p * (dout[:, h] @ v[:, g].T - (dout[:, h] * o).sum(axis=1, keepdims=True))
+        tq[:, h] = scale * np.abs(ds) @ np.abs(k[:, g])
+        tk[:, g] += scale * np.abs(ds).T @ np.abs(q[:, h])
+        tv[:, g] += p.T @ np.abs(dout[:, h])
+    return tq[None], tk[None], tv[None]
+
+
+def _excess(got, ref, terms, tol, rel):
+    """Largest error beyond the elementwise bound tol * max(1, max|ref|) +
+    rel * terms (<= 0 when every element is inside it)."""
+    bound = tol * max(1.0, float(np.abs(ref).max(initial=0.0))) + rel * terms
+    return float((np.abs(got - ref) - bound).max(initial=-1.0))
+
+
+@pytest.mark.parametrize("dtype,layout,rising", [
+    ("bf16", "contiguous", True),
+    ("bf16", "striped", True),
+    ("bf16", "zigzag", False),
+    ("f32", "contiguous", True),
+])
+def test_ring_backward_with_moving_maximum(dtype, layout, rising):
+    """Forward and backward of every rank under a score ramp (causal): dq per
+    rank, dk and dv summed over the ranks, against the plain gradient, element
+    by element within tol * max(1, max|ref|) + rel * (that element's summed
+    terms, _term_scales): tol 1e-2 and rel 2^-8 for bfloat16 (P and dS are
+    rounded to bfloat16, 2^-9 each); tol 1e-5 and rel 4 * 2^-24 * max|s| for
+    float32 (the scores' own rounding, carried by every weight)."""
+    n, blen, hq, hkv, d = 4, 128, 4, 2, 128
+    say(f"ramp backward: {dtype} {layout} rising={rising}")
+    q, k, v = _ramp(13, n * blen, hq, hkv, d, 120.0, rising, dtype)
+    g = torch.Generator().manual_seed(3)
+    dout_g = torch.randn(q.shape, generator=g).to(q.dtype).to(DEV)
+    rq, rk, rv = orc.naive_attention_grad(_np64(q), _np64(k), _np64(v), _np64(dout_g), True)
+    sq, sk, sv = _term_scales(q, k, v, dout_g, True)
+    if dtype == "f32":
+        tol, rel = TOL[torch.float32], _f32_bounds(q, k, v)[1] - LSE_TOL["f32"]
+    else:
+        tol, rel = TOL[torch.bfloat16], 2.0 ** -8
+    kb, vb = blocks_from_global(k, layout, n), blocks_from_global(v, layout, n)
+    dk = torch.zeros(kb.shape, dtype=torch.float32, device=DEV)
+    dv = torch.zeros(vb.shape, dtype=torch.float32, device=DEV)
+    for r in range(n):
+        rows = share_tokens(layout, n, r, blen).to(DEV)
+        qs, dout = q[:, rows].contiguous(), dout_g[:, rows].contiguous()
+        out, lse = B.ra_ring_fwd(qs, kb, vb, n_ring=n, causal=True, layout=layout, rank=r)
+        dq, _, _ = B.ra_ring_bwd(qs, kb, vb, out, dout, lse, n_ring=n, causal=True, layout=layout,
+                                 rank=r, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        idx = rows.cpu().numpy()
+        x = _excess(_np64(dq), rq[:, idx], sq[:, idx], tol, rel)
+        assert x <= 0, ("dq", r, x)
+    for j in range(n):
+        keys = share_tokens(layout, n, j, blen).numpy()
+        x_k = _excess(_np64(dk[j]), rk[:, keys], sk[:, keys], tol, rel)
+        x_v = _excess(_np64(dv[j]), rv[:, keys], sv[:, keys], tol, rel)
+        assert x_k <= 0, ("dk", j, x_k)
+        assert x_v <= 0, ("dv", j, x_v)
