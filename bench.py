@@ -382,9 +382,10 @@ def backward_leg(dev, layouts, reps=1):
     return res
 
 
-def load_counters(src_hash):
-    """HBM traffic per attention launch from committed rocprofv3 counter runs,
-    only if they were taken on the current kernel source."""
+def load_counters(src_hash, kernel="attention"):
+    """HBM traffic per launch of the attention kernel (or, kernel="merge", of
+    the merge kernel) from committed rocprofv3 counter runs, only if they
+    were taken on the current kernel source."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
@@ -392,6 +393,8 @@ def load_counters(src_hash):
         return None
     if c.get("kernel_source_hash") != src_hash:
         return None
+    if kernel == "merge":
+        return (c.get("merge") or {}).get("hbm_bytes_per_launch")
     return c.get("hbm_bytes_per_launch")
 
 
@@ -570,6 +573,8 @@ def main():
             del w2, out2, lse2, ws2
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
+        # measured HBM bytes per merge at this share (counters), if current
+        result["merge"]["traffic"] = load_counters(src_hash, "merge") if args.workload == "c4" else None
         log("[bench] merge leg done")
         if args.workload == "c4" and not args.skip_aux and not args.skip_backward:
             result["backward"] = backward_leg(dev, layouts)

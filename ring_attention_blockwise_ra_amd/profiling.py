@@ -98,8 +98,12 @@ def _counter_values(run_dir: str, counter: str):
     return out
 
 
+MERGE = "merge_partials_kernel"
+
+
 def traffic(fetch_dir: str, write_dir: str, calib_bytes: int) -> dict:
     res = {}
+    merge = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _counter_values(d, counter)
         copies = [v for n, v in vals.values() if COPY in n]
@@ -111,8 +115,15 @@ def traffic(fetch_dir: str, write_dir: str, calib_bytes: int) -> dict:
         per_launch = sum(attn) / len(attn) * 1024.0 * factor
         res[counter] = dict(calib_kib=calib_kib, factor=factor, launches=len(attn),
                             bytes_per_launch=per_launch)
+        mg = [v for n, v in vals.values() if MERGE in n]
+        if mg:
+            merge[counter] = dict(launches=len(mg), bytes_per_launch=sum(mg) / len(mg) * 1024.0 * factor)
     res["hbm_bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + \
         res["WRITE_SIZE"]["bytes_per_launch"]
+    if len(merge) == 2:  # the merge kernel's measured HBM bytes, same scaling
+        merge["hbm_bytes_per_launch"] = merge["FETCH_SIZE"]["bytes_per_launch"] + \
+            merge["WRITE_SIZE"]["bytes_per_launch"]
+        res["merge"] = merge
     return res
 
 

@@ -51,7 +51,9 @@ def test_traffic_scales_by_calibration_copy(tmp_path):
         # the second attention dispatch reports two instances that are summed
         rows += [dict(Dispatch_Id=3, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[0]),
                  dict(Dispatch_Id=4, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[1] / 2),
-                 dict(Dispatch_Id=4, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[1] / 2)]
+                 dict(Dispatch_Id=4, Kernel_Name=attn, Counter_Name=counter, Counter_Value=per[1] / 2),
+                 dict(Dispatch_Id=5, Kernel_Name="ra::merge_partials_kernel(long)", Counter_Name=counter,
+                      Counter_Value=64.0)]
         _write(str(tmp_path / d / "x_counter_collection.csv"), rows)
     t = P.traffic(str(tmp_path / "f"), str(tmp_path / "w"), 1 << 30)
     # FETCH reads 2 GiB for the 1 GiB copy: factor 1/2
@@ -59,6 +61,8 @@ def test_traffic_scales_by_calibration_copy(tmp_path):
     assert t["FETCH_SIZE"]["bytes_per_launch"] == pytest.approx(400.0 * 1024 * 0.5)
     assert t["WRITE_SIZE"]["bytes_per_launch"] == pytest.approx(100.0 * 1024)
     assert t["hbm_bytes_per_launch"] == pytest.approx(400.0 * 512 + 100.0 * 1024)
+    assert t["merge"]["FETCH_SIZE"]["launches"] == 1
+    assert t["merge"]["hbm_bytes_per_launch"] == pytest.approx(64.0 * 512 + 64.0 * 1024)
 
 
 def test_sq_summary_busy_fraction_and_clock(tmp_path):
