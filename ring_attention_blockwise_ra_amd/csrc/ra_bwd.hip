@@ -223,6 +223,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16(BwdParams p) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[c], dqa[db], 0, 0, 0);
     }
+    // scheduling hint: LDS operand reads interleaved with the MFMAs (as in
+    // the forward kernel; about 1 % here)
+    __builtin_amdgcn_iglp_opt(0);
   };
 
   if (n_kt > 0) {
@@ -655,6 +658,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
       weights(std::false_type{}, tt, s_cur, dp_cur, pb, dsb);
       scores(tt + 1, s_nxt, dp_nxt);
       accumulate(tt, pb, dsb);
+      // scheduling hint for the step's region (the compiler's second
+      // interleave strategy; 1-4 % here, while the first one is 20 % slower)
+      __builtin_amdgcn_iglp_opt(2);
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
     };
     const int e1 = max(t_first, min(t_full, n_rt));

@@ -253,6 +253,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
     if (has_next) qk(sn, u + 1);
     softmax_p(sc, pcur);
     if (has_prev) pv(pprev, u - 1);
+    // Scheduling hint for this unit's region: the compiler's "small GEMM"
+    // interleave, which issues the LDS operand reads in pairs one MFMA ahead
+    // of the MFMA that consumes them (measured 4 % faster than its default
+    // order on a 131072-key block; the arithmetic is unchanged).
+    __builtin_amdgcn_iglp_opt(0);
     rescale_o(alpha);
   };
 
