@@ -2,7 +2,7 @@
 
     python -m ring_attention_blockwise_ra_amd.profiling trace  <kernel_trace.csv> <kernel_stats.csv>
     python -m ring_attention_blockwise_ra_amd.profiling traffic <fetch_dir> <write_dir> <out.json>
-    python -m ring_attention_blockwise_ra_amd.profiling sq <pmc_dir>
+    python -m ring_attention_blockwise_ra_amd.profiling sq <pmc_dir> [kernel name part]
 
 trace:   per-kernel statistics of the attention, merge and finalize kernels,
          and how much of the side-queue staging copy time ran while an
@@ -183,7 +183,7 @@ def main(argv):
             json.dump(t, f, indent=1)
         print(json.dumps(t, indent=1))
     elif len(argv) >= 2 and argv[0] == "sq":
-        print(json.dumps(sq_summary(argv[1]), indent=1))
+        print(json.dumps(sq_summary(argv[1], *argv[2:3]), indent=1))
     else:
         print(__doc__)
         return 2
