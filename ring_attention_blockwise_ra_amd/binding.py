@@ -266,7 +266,8 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
     if need == 0 and b * lq * hq > 0:
         _check(lib().ra_ring_fwd(ctypes.byref(prob), None, None, None, None, None, None, 0,
                                  None, None))
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, device=dev)
     with torch.cuda.device(dev):
@@ -277,6 +278,8 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
         _check(lib().ra_ring_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                  _ptr(lse), _ptr(workspace), workspace.numel(),
                                  ctypes.c_void_p(cs.cuda_stream), xs))
+        if own_ws:
+            _record(workspace, cs, copy_stream)
     return out, lse
 
 
@@ -357,7 +360,8 @@ def ra_ring_bwd(q, k, v, out, dout, lse, *, n_ring: int, causal: bool, layout="c
     if need == 0 and b * lq * hq > 0:
         _check(lib().ra_ring_bwd(ctypes.byref(prob), None, None, None, None, None, None, None,
                                  None, None, None, 0, None, None))
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, device=dev)
     with torch.cuda.device(dev):
@@ -369,6 +373,8 @@ def ra_ring_bwd(q, k, v, out, dout, lse, *, n_ring: int, causal: bool, layout="c
                                  _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(workspace), workspace.numel(),
                                  ctypes.c_void_p(cs.cuda_stream), xs))
+        if own_ws:
+            _record(workspace, cs, copy_stream)
     return dq, dk, dv
 
 
@@ -394,6 +400,16 @@ def ra_rope_apply(x, prob: RaProblem, *, target="keys", block_j: int = 0, out=No
 
 
 _side = {}
+
+
+def _record(t, *streams):
+    """Keep an internally allocated device buffer reserved until the work
+    enqueued on `streams` (the ring's compute and copy streams) has run: the
+    caching allocator otherwise only orders its reuse after the stream it was
+    allocated on (the current one)."""
+    for st in streams:
+        if isinstance(st, torch.cuda.Stream):
+            t.record_stream(st)
 
 
 def side_stream(device) -> torch.cuda.Stream:
