@@ -29,6 +29,7 @@
 
 #include <mutex>
 #include <set>
+#include <type_traits>
 #include <utility>
 
 #include "ra_device.h"
@@ -67,16 +68,85 @@ namespace ra {
 // 16-bit element of the 8 bytes addressed by source lane 4j + i/4. Source lane
 // s therefore addresses V[k0 + s/4][d0 + 4(s%4)], and output lane i receives
 // V[k0 .. k0+3][d0 + i]: four consecutive keys of one head dimension.
+//
+// LDS holds kSlots K tiles, then kSlots V tiles. For D = 128 with 8 waves a
+// tile uses the padded layout below instead of the XOR-swizzled rows of
+// BfTile: every operand read of a lane is then its one base address plus an
+// immediate offset (no address arithmetic per read, 10 fewer VGPRs).
+
+// D = 128 tile: rows in groups of 4 (one 1 KiB DMA instruction each), group j
+// at j * SEGP bytes (64 bytes of padding per group). Inside a group the
+// 16-byte granule 16*(c/4) + 4*r + c%4 holds chunk c (head dims 8c..8c+7) of
+// row 4j + r. The padding of 4 granules rotates the banks by one granule per
+// group, which keeps both operand reads conflict-free: a K read (16 lanes of
+// 16 bytes, rows 0..15 of one chunk) and a transposed V read (32 lanes of 8
+// bytes, 4 rows x 4 chunks) each cover all 64 banks once. Chunk c of row r
+// lies at (r/4)*SEGP + 16*(16*(c/4) + 4*(r%4) + c%4), affine in c inside
+// each run of 4 chunks, so the reads of successive MFMA steps differ by
+// constants. Each group of 4 DMA lanes reads 64 contiguous bytes of one row.
+struct KvTile128 {
+  static constexpr int SEGP = 1040;
+  static constexpr int TB = 16 * SEGP;   // 64 keys
+  static constexpr int HALF = 8 * SEGP;  // 32 keys
+};
+
+// Global -> LDS copies of one tile in the KvTile128 layout (the same contract
+// as KvTileDma: fixed per-lane offsets, the last key re-read past kv_len,
+// tiles past the last one reload it, LPW loads per wave per tile).
+template <int NW>
+struct KvTileDma128 {
+  static constexpr int LPW = 16 / NW;
+  uint32_t off[LPW], off_last[LPW];
+  int seg[LPW];
+  int n_real;
+  int64_t tile_elems;
+  __device__ __forceinline__ KvTileDma128(int kv_len, int row_stride, int wave, int lane) {
+    n_real = (kv_len + kTK - 1) / kTK;
+    tile_elems = (int64_t)kTK * row_stride;
+    const int last_row = kv_len - (n_real - 1) * kTK - 1;
+    // lane l writes granule l of its group: chunk 4*(l/16) + l%4 of row (l/4)%4
+    const int c = 4 * (lane >> 4) + (lane & 3), r4 = (lane >> 2) & 3;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int sg = (wave + j * NW) % 16;
+      const int row = 4 * sg + r4;
+      seg[j] = sg * KvTile128::SEGP;
+      off[j] = (uint32_t)(row * row_stride + c * 8) * 2u;
+      off_last[j] = (uint32_t)(min(row, last_row) * row_stride + c * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t* src, int t, char* dst) const {
+    const int te = min(t, n_real - 1);
+    const bool last = te == n_real - 1;
+    const uint16_t* base = src + te * tile_elems;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) lds_dma_off<16>(base, last ? off_last[j] : off[j], dst + seg[j]);
+  }
+};
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
+constexpr bool kPadTile = D == 128 && NW == 8;
+
+// The kernel's dynamic LDS (K/V tile ring) is sized at launch, so the
+// compiler cannot see that it limits the kernel to one workgroup per CU; with
+// 8 waves that is two waves per SIMD, which is stated here so that the
+// scheduler plans for up to 256 VGPRs rather than serialising operand reads
+// to free registers for an occupancy the LDS never allows.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(kPadTile<D, NW> ? 2 : 1, kPadTile<D, NW> ? 2 : 8)))
+void attn_bf16_mfma(AttnParams p) {
   using T = BfTile<D>;
   constexpr int ROWS = 32 * NW;
   constexpr int KSTEPS = D / 16;
   constexpr int KB = kTK / 32;   // 32-key blocks per tile
   constexpr int KC = kTK / 16;   // 16-key chunks per tile
   constexpr int DB = T::DP / 32; // 32-dim blocks of the output
-  constexpr int LOADS_PER_TILE = 2 * KvTileDma<D, NW>::LPW;  // per wave: K and V
+  constexpr bool PAD = kPadTile<D, NW>;
+  using Dma = std::conditional_t<PAD, KvTileDma128<NW>, KvTileDma<D, NW>>;
+  constexpr int TBX = PAD ? KvTile128::TB : T::TB;                // bytes per K (or V) tile
+  constexpr int HALFX = PAD ? KvTile128::HALF : 32 * T::ROWB;     // bytes per 32 keys
+  constexpr int LOADS_PER_TILE = 2 * Dma::LPW;  // per wave: K and V
 
   extern __shared__ __align__(16) char smem[];
 
@@ -141,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   // K operand, step t: row col (+32 per half tile), chunk 2t + half; f
   // depends on the row modulo 16, so the +32 row offset keeps it.
   int koff[KSTEPS];
-  {
+  if constexpr (!PAD) {
     const int fr = swz(col) & (T::CPR - 1);
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) koff[t] = col * T::ROWB + (((2 * t + half) ^ fr) & (T::CPR - 1)) * 16;
@@ -150,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   // +32 per half tile) and r + 8 (the second read of an operand), head dims
   // db*32 + 16*(grp%2) + 4*(sl%4) .. +3, i.e. chunk 4 db + 2*(grp%2) + (sl/2)%2.
   int voff[DB], voff8[DB];
-  {
+  if constexpr (!PAD) {
     const int grp = lane >> 4, sl = lane & 15;
     const int r = 4 * (grp >> 1) + (sl >> 2);
     const int lowc = 2 * (grp & 1) + ((sl >> 1) & 1);
@@ -168,30 +238,45 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   // keeps the O rescale (a multiply per accumulator) off most units.
   float base = kNegInf;
 
-  auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT; };
-  auto slot_v = [&](int t) { return smem + (t & (kSlots - 1)) * T::SLOT + T::TB; };
-  const KvTileDma<D, NW> kv_dma(kv_len, kv_row_stride, wave, lane);
+  // Padded layout: K step t (chunk 2t + half of row col) at kbase + 256*(t/2)
+  // + 32*(t%2); V^T read (db, chunk c) at vbase + 4*SEGP*c + 256*db, its second
+  // half 8 rows (2 groups) further.
+  int kbase = 0, vbase = 0;
+  if constexpr (PAD) {
+    kbase = (col >> 2) * KvTile128::SEGP + 16 * (4 * (col & 3) + half);
+    const int grp = lane >> 4, sl = lane & 15;
+    const int lowc = 2 * (grp & 1) + ((sl >> 1) & 1);
+    vbase = (grp >> 1) * KvTile128::SEGP + 16 * (4 * (sl >> 2) + lowc) + 8 * (sl & 1);
+  }
+
+  auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * TBX; };
+  auto slot_v = [&](int t) { return smem + (kSlots + (t & (kSlots - 1))) * TBX; };
+  const Dma kv_dma(kv_len, kv_row_stride, wave, lane);
   auto issue = [&](int t) {
     kv_dma.issue(kg, t, slot_k(t));
     kv_dma.issue(vg, t, slot_v(t));
   };
   // Work is done in units of 32 keys: unit u is half u%2 of tile u/2. S(u)
   // is one 32x32 MFMA tile (16 registers per lane), P(u) two bf16x8 operands.
-  auto qk = [&](f32x16& s_out, int u) {
-    const char* sK = slot_k(u >> 1) + (u & 1) * 32 * T::ROWB;
+  // ks / vs: the LDS slot holding tile u/2 (the caller knows it).
+  auto qk = [&](f32x16& s_out, int u, int ks) {
+    const char* sK = slot_k(ks) + (u & 1) * HALFX;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + koff[t]);
+      const char* pa = PAD ? sK + kbase + 256 * (t >> 1) + 32 * (t & 1) : sK + koff[t];
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(pa);
       s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? f32x16{} : s_out, 0, 0, 0);
     }
   };
-  auto pv = [&](const bf16x8 (&pf)[2], int u) {
-    const char* sV = slot_v(u >> 1) + (u & 1) * 32 * T::ROWB;
+  auto pv = [&](const bf16x8 (&pf)[2], int u, int vs) {
+    const char* sV = slot_v(vs) + (u & 1) * HALFX;
 #pragma unroll
     for (int j = 0; j < 2 * DB; ++j) {
       const int db = j >> 1, c = j & 1;
-      const s16x4 lo = lds_read_tr16(sV + voff[db] + (c * 16) * T::ROWB);
-      const s16x4 hi = lds_read_tr16(sV + voff8[db] + (c * 16) * T::ROWB);
+      const char* plo = PAD ? sV + vbase + 4 * KvTile128::SEGP * c + 256 * db : sV + voff[db] + (c * 16) * T::ROWB;
+      const char* phi = PAD ? plo + 2 * KvTile128::SEGP : sV + voff8[db] + (c * 16) * T::ROWB;
+      const s16x4 lo = lds_read_tr16(plo);
+      const s16x4 hi = lds_read_tr16(phi);
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], oacc[db], 0, 0, 0);
     }
@@ -248,11 +333,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
   // O += V(u-1) P(u-1). None of these MFMAs depends on the exponentials of
   // the same unit, so the matrix core and the transcendental unit overlap.
   auto unit = [&](f32x16& sc, f32x16& sn, const bf16x8 (&pprev)[2], bf16x8 (&pcur)[2], int u,
-                  bool has_next, bool has_prev) {
+                  bool has_next, bool has_prev, int ks, int vs) {
     const float alpha = mask_and_ref(sc, u);
-    if (has_next) qk(sn, u + 1);
+    if (has_next) qk(sn, u + 1, ks);
     softmax_p(sc, pcur);
-    if (has_prev) pv(pprev, u - 1);
+    if (has_prev) pv(pprev, u - 1, vs);
     // Scheduling hint for this unit's region: the compiler's "small GEMM"
     // interleave, which issues the LDS operand reads in pairs one MFMA ahead
     // of the MFMA that consumes them (measured 4 % faster than its default
@@ -279,30 +364,32 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_mfma(AttnParams p) {
     const int n_u = (key_end + 31) / 32;  // units with any visible key
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
-    qk(sA, 0);
-    unit(sA, sB, pB, pA, 0, n_u > 1, false);  // S(1) -> sB, P(0) -> pA
+    qk(sA, 0, 0);
+    unit(sA, sB, pB, pA, 0, n_u > 1, false, 0, 0);  // S(1) -> sB, P(0) -> pA
     int t = 0;
     for (; 2 * t + 3 < n_u; ++t) {
       issue(t + 3);
-      unit(sB, sA, pA, pB, 2 * t + 1, true, true);  // S(2t+2) -> sA, P(2t+1) -> pB
-      unit(sA, sB, pB, pA, 2 * t + 2, true, true);  // S(2t+3) -> sB, P(2t+2) -> pA
+      const int s0 = t & (kSlots - 1), s1 = (t + 1) & (kSlots - 1);
+      unit(sB, sA, pA, pB, 2 * t + 1, true, true, s1, s0);  // S(2t+2) -> sA, P(2t+1) -> pB
+      unit(sA, sB, pB, pA, 2 * t + 2, true, true, s1, s0);  // S(2t+3) -> sB, P(2t+2) -> pA
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
     }
     // tail: units 2t+1 .. n_u-1 (at most two); every tile they read has
     // landed once this wave's loads are complete and all waves met
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     int u = 2 * t + 1;
+    const int s0 = t & (kSlots - 1), s1 = (t + 1) & (kSlots - 1);
     if (u < n_u) {
-      unit(sB, sA, pA, pB, u, u + 1 < n_u, true);
+      unit(sB, sA, pA, pB, u, u + 1 < n_u, true, s1, s0);
       ++u;
       if (u < n_u) {
-        unit(sA, sB, pB, pA, u, false, true);
-        pv(pA, u);
+        unit(sA, sB, pB, pA, u, false, true, s1, s0);
+        pv(pA, u, s1);
       } else {
-        pv(pB, u - 1);
+        pv(pB, u - 1, s0);
       }
     } else {
-      pv(pA, u - 1);
+      pv(pA, u - 1, s0);
     }
   }
 
@@ -559,7 +646,8 @@ template <int D, int NW>
 static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
   constexpr int ROWS = 32 * NW;
   const int64_t tiles = set_tiles(p, ROWS);
-  const size_t smem = kSlots * BfTile<D>::SLOT;  // ring of K/V tile slots
+  // ring of kSlots K tiles and kSlots V tiles
+  const size_t smem = 2 * kSlots * (size_t)(kPadTile<D, NW> ? KvTile128::TB : BfTile<D>::TB);
   auto kern = attn_bf16_mfma<D, NW>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
   if (e != hipSuccess) return e;
