@@ -211,6 +211,37 @@ def test_ring_poisoned_workspace_and_delayed_copy_stream():
         assert torch.equal(out, ref)
 
 
+def test_ring_on_a_side_compute_stream_keeps_its_own_workspace():
+    """The ring runs on a compute stream that is not the current one, held
+    back by a spin, with the workspace allocated inside the call. Buffers of
+    the same size allocated and NaN-filled on the current stream right after
+    the call must not land on that workspace while the ring still uses it."""
+    say("ring: internal workspace on a non-current compute stream")
+    n, blen, hq, hkv, d = 4, 512, 8, 2, 128
+    qg, kg, vg = _rand_global(6, 1, n * blen, hq, hkv, d, "bf16")
+    kb, vb = blocks_from_global(kg, "striped", n), blocks_from_global(vg, "striped", n)
+    r = 3
+    q = qg[:, share_tokens("striped", n, r, blen).to(DEV)].contiguous()
+    prob = B.make_problem(dtype=torch.bfloat16, batch=1, hq=hq, hkv=hkv, head_dim=d, q_len=blen,
+                          kv_len=blen, n_ring=n, rank=r, causal=True, layout="striped")
+    need = B.ra_ring_workspace_bytes(prob)
+    ref, _ = B.ra_ring_fwd(q, kb, vb, n_ring=n, causal=True, layout="striped", rank=r)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    for _ in range(3):
+        cs.wait_stream(torch.cuda.current_stream())
+        if hasattr(torch.cuda, "_sleep"):
+            with torch.cuda.stream(cs):
+                torch.cuda._sleep(2_000_000)
+        out, _ = B.ra_ring_fwd(q, kb, vb, n_ring=n, causal=True, layout="striped", rank=r,
+                               compute_stream=cs)
+        junk = [torch.full((max(need, 1),), 0xFF, dtype=torch.uint8, device=DEV) for _ in range(2)]
+        torch.cuda.synchronize()
+        del junk
+        assert torch.isfinite(out).all()
+        assert torch.equal(out, ref)
+
+
 # ---------------------------------------------------------------- invariants
 def test_causal_row0_and_constant_keys_on_gpu():
     say("invariants: row 0 = V[0]; constant keys = mean of visible V")
