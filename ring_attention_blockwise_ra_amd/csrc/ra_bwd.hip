@@ -316,6 +316,7 @@ __device__ __forceinline__ int first_row_seeing(BlockGeom geom, int k0, int n_ro
 
 constexpr int kRT = 32;        // query rows per row tile of the dk/dv kernel
 constexpr int kRowSlots = 4;   // LDS ring of row tiles; loads run 3 tiles ahead
+constexpr int kRowSegP = 1040; // bytes per padded group of 4 rows (d = 128)
 
 template <int D>
 struct RowTile {
@@ -336,6 +337,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = T::DP / 32;
   constexpr int KEYS = 32 * NW;
+  // d = 128: row tiles in the forward kernel's padded layout (rows in groups
+  // of 4, one 1 KiB DMA instruction each, group j at j * kRowSegP bytes; the
+  // 16-byte granule 16*(c/4) + 4*r + c%4 holds chunk c of row 4j + r), so
+  // every Q / dO operand read is one base register plus an immediate offset
+  // and stays bank-conflict free. Other head sizes: XOR-swizzled rows.
+  constexpr bool PR = D == 128;
+  constexpr int TBR = PR ? (kRT / 4) * kRowSegP : R::TB;  // bytes of one Q (or dO) row tile
+  constexpr int SLOTR = 2 * TBR;
   constexpr int LPW = (R::SEGS + NW - 1) / NW;
   constexpr int LOADS_PER_TILE = 2 * LPW + 1;  // per wave: Q, dO and the row statistics
 
@@ -347,8 +356,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave limits stay scalar
   const int half = lane >> 5;
   const int col = lane & 31;
-  float* stats = reinterpret_cast<float*>(smem + kRowSlots * R::SLOT) + wave * kRowSlots * 64;
-  int* elim = reinterpret_cast<int*>(smem + kRowSlots * R::SLOT + NW * kRowSlots * 64 * 4) + wave * 32;
+  float* stats = reinterpret_cast<float*>(smem + kRowSlots * SLOTR) + wave * kRowSlots * 64;
+  int* elim = reinterpret_cast<int*>(smem + kRowSlots * SLOTR + NW * kRowSlots * 64 * 4) + wave * 32;
 
   const KeyTileRef kr = locate_key_tile(p);
   const int b = kr.b, g = kr.g;
@@ -415,8 +424,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   }
   const float sl2 = p.scale_log2;
 
-  auto slot_q = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT; };
-  auto slot_o = [&](int t) { return smem + (t & (kRowSlots - 1)) * R::SLOT + R::TB; };
+  auto slot_q = [&](int t) { return smem + (t & (kRowSlots - 1)) * SLOTR; };
+  auto slot_o = [&](int t) { return smem + (t & (kRowSlots - 1)) * SLOTR + TBR; };
+  // padded layout: S / dP step k reads qbase + 256*(k/2) + 32*(k%2); the
+  // transposed read (db, chunk c) vbase + 4*kRowSegP*c + 256*db, its second
+  // half two groups (8 rows) further
+  int qbase = 0, vbase = 0;
+  if constexpr (PR) {
+    qbase = (col >> 2) * kRowSegP + 16 * (4 * (col & 3) + half);
+    const int g16 = lane >> 4, sl = lane & 15;
+    const int lowc = 2 * (g16 & 1) + ((sl >> 1) & 1);
+    vbase = (g16 >> 1) * kRowSegP + 16 * (4 * (sl >> 2) + lowc) + 8 * (sl & 1);
+  }
   auto slot_s = [&](int t) { return stats + (t & (kRowSlots - 1)) * 64; };
 
   // Row cursors of the DMA (groups that do not divide the row tile): row rho
@@ -432,13 +451,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   int c_rho[LPW_R + 1], c_a[LPW_R + 1], c_h[LPW_R + 1];
   int dma_off[LPW_R], dma_lc[LPW_R];
   {
-    const int rin = lane / R::CPR, pc = lane % R::CPR;
+    // padded: lane l writes granule l of its group, chunk 4*(l/16) + l%4 of row (l/4)%4
+    const int rin = PR ? (lane >> 2) & 3 : lane / R::CPR, pc = lane % R::CPR;
 #pragma unroll
     for (int j = 0; j < LPW_R; ++j) {
       const int seg = (wave + j * NW) % R::SEGS;
       const int row = seg * R::ROWS_PER_SEG + rin;
-      dma_off[j] = seg * 1024;
-      dma_lc[j] = (pc ^ (swz(row) & (R::CPR - 1))) * 8;
+      dma_off[j] = seg * (PR ? kRowSegP : 1024);
+      dma_lc[j] = PR ? (4 * (lane >> 4) + (lane & 3)) * 8 : (pc ^ (swz(row) & (R::CPR - 1))) * 8;
       c_rho[j] = t_first * kRT + row;
     }
     c_rho[LPW_R] = t_first * kRT + col;  // the statistics of row col
@@ -474,7 +494,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
   const int vr = rows_total - (n_rt - 1) * kRT;  // valid rows of the last tile
   uint32_t ro[LPW_R + 1], ro_last[LPW_R + 1];
   if constexpr (REG) {
-    const int rin = lane / R::CPR;
+    const int rin = PR ? (lane >> 2) & 3 : lane / R::CPR;
 #pragma unroll
     for (int j = 0; j <= LPW_R; ++j) {
       // Q / dO rows (j < LPW_R): bytes of the (query, head) row plus the
@@ -550,12 +570,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
     const char* sO = slot_o(t);
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + qoff[k]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(PR ? sQ + qbase + 256 * (k >> 1) + 32 * (k & 1) : sQ + qoff[k]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[k], k == 0 ? f32x16{} : s, 0, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sO + qoff[k]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(PR ? sO + qbase + 256 * (k >> 1) + 32 * (k & 1) : sO + qoff[k]);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[k], k == 0 ? f32x16{} : dp, 0, 0, 0);
     }
   };
@@ -607,12 +627,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < 2 * DB; ++j) {
       const int db = j >> 1, c = j & 1;
-      const s16x4 olo = lds_read_tr16(sO + voff[db] + (c * 16) * R::ROWB);
-      const s16x4 ohi = lds_read_tr16(sO + voff8[db] + (c * 16) * R::ROWB);
+      const int vlo = PR ? vbase + 4 * kRowSegP * c + 256 * db : voff[db] + (c * 16) * R::ROWB;
+      const int vhi = PR ? vlo + 2 * kRowSegP : voff8[db] + (c * 16) * R::ROWB;
+      const s16x4 olo = lds_read_tr16(sO + vlo);
+      const s16x4 ohi = lds_read_tr16(sO + vhi);
       const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
       dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[c], dva[db], 0, 0, 0);
-      const s16x4 qlo = lds_read_tr16(sQ + voff[db] + (c * 16) * R::ROWB);
-      const s16x4 qhi = lds_read_tr16(sQ + voff8[db] + (c * 16) * R::ROWB);
+      const s16x4 qlo = lds_read_tr16(sQ + vlo);
+      const s16x4 qhi = lds_read_tr16(sQ + vhi);
       const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
       dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[c], dka[db], 0, 0, 0);
     }
@@ -925,7 +947,8 @@ static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
   {
     BwdParams q = p;
     const int64_t tiles = set_tiles_bwd(q, 32 * kKvWaves, true);
-    const size_t smem = kRowSlots * RowTile<D>::SLOT + kKvWaves * (kRowSlots * 64 + 32) * 4;
+    const size_t rslot = D == 128 ? 2 * (kRT / 4) * kRowSegP : RowTile<D>::SLOT;  // padded rows at d = 128
+    const size_t smem = kRowSlots * rslot + kKvWaves * (kRowSlots * 64 + 32) * 4;
     const bool reg = kRT % q.group == 0;
     auto kern = reg ? bwd_dkdv_bf16<D, kKvWaves, true> : bwd_dkdv_bf16<D, kKvWaves, false>;
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
