@@ -4,7 +4,9 @@ The kernel (`ra_kernels.hip`: `KvTile128`, `KvTileDma128` and the operand
 reads of `attn_bf16_mfma`, and `BfTile` / `swz` in `ra_device.h`) places each
 64-key K or V tile in LDS so that the two operand reads of the MFMAs are free
 of bank conflicts. The formulas below restate the kernel's per-lane address
-arithmetic; the tests enumerate every lane and step and check that
+arithmetic (the dk/dv kernel of `ra_bwd.hip` stores its 32-row Q / dO tiles
+in the same padded groups and reads them with the same formulas, which are
+the half-tile-0 cases here); the tests enumerate every lane and step and check that
 
 * each read lands on the key row and head dims the MFMA formulation needs
   (K operand: row `col` + 32 per half tile, chunk 2t + half; transposed V
