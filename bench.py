@@ -12,9 +12,13 @@ striped. Inputs are resident in HBM before timing starts.
 Printed (one JSON line): TFLOP/s over causal-counted FLOPs (4*d per visible
 (query, key) pair per query head), the roofline of the attention kernel
 (its FLOPs per launch over its average launch time, measured with HIP events
-on its own stream), copy/compute overlap of the staged ring, merge-kernel
-HBM bandwidth, and the fp64 CPU oracle timed on a bounded sample of the same
-workload (a reported baseline, not a target).
+on its own stream), the cost of the staging copies (staged ring against the
+same kernels reading every block in place, interleaved pairs), merge-kernel
+HBM bandwidth, the backward ring, the other workloads' ring TFLOP/s (the
+8192-token sequence, the 131072-token striped share at every rank, the
+921,600-token video share), and the fp64 CPU oracle timed on a bounded sample
+of the same workload (a reported baseline, not a target) together with the
+max-abs error of the GPU output on those sampled rows (`parity`).
 """
 
 from __future__ import annotations
@@ -189,10 +193,17 @@ def captured(fn):
     return g.replay
 
 
-def overlap_leg(w, out, lse, ws, reps=3, graph=False):
-    """T_ring (copies on a side stream), T_nocopy (same kernels reading the
-    source blocks in place, through the public entry points), T_copy (the
-    N-1 staging copies alone). efficiency = 1 - max(0, T_ring - T_nocopy)/T_copy.
+def overlap_leg(w, out, lse, ws, reps=11, graph=False, copy_stream="auto"):
+    """Cost of the staging copies: T_ring (the ring as the library runs it:
+    copies on a side stream, or in order for small blocks), T_nocopy (the
+    same kernels through the public entry points, every block read in place
+    from the sources), T_copy (the N-1 staging copies alone).
+
+    The ring and the no-copy sequence are timed in `reps` interleaved pairs,
+    so clock drift hits both alike; the cost is the median of the paired
+    differences T_ring - T_nocopy, reported with its quartiles and range.
+    efficiency = 1 - max(0, median difference) / T_copy: 1 when the copies
+    cost nothing, 0 when they cost as much as running them alone.
     graph: the ring and the no-copy sequence are each captured in a HIP graph
     and replayed (no per-launch host cost)."""
     c = w["cfg"]
@@ -226,19 +237,25 @@ def overlap_leg(w, out, lse, ws, reps=3, graph=False):
             stage_k.copy_(w["k"][j])
             stage_v.copy_(w["v"][j])
 
-    ring_fn, nocopy_fn = (lambda: ring_call(w, out, lse, ws)), nocopy
+    ring_fn = lambda: ring_call(w, out, lse, ws, copy_stream=copy_stream)  # noqa: E731
+    nocopy_fn = nocopy
     if graph:
         ring_fn, nocopy_fn = captured(ring_fn), captured(nocopy_fn)
     tr, tn = [], []
-    for _ in range(reps):  # interleaved, so clock drift hits both alike
+    for _ in range(reps):
         tr.append(timed(ring_fn))
         tn.append(timed(nocopy_fn))
-    t_ring, t_nocopy = sorted(tr)[len(tr) // 2], sorted(tn)[len(tn) // 2]
-    t_copy = min(timed(copies) for _ in range(reps))
-    eff = 1.0 - max(0.0, t_ring - t_nocopy) / t_copy if t_copy > 0 else 1.0
-    return dict(efficiency=round(eff, 4), t_ring_ms=round(t_ring, 3),
-                t_nocopy_ms=round(t_nocopy, 3), t_copy_ms=round(t_copy, 3),
-                ring_spread_ms=round(max(tr) - min(tr), 3),
+    diffs = sorted(a - b for a, b in zip(tr, tn))
+    q_ = lambda xs, f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]  # noqa: E731
+    med = q_(diffs, 0.5)
+    t_copy = sorted(timed(copies) for _ in range(5))[2]
+    eff = 1.0 - max(0.0, med) / t_copy if t_copy > 0 else 1.0
+    return dict(efficiency=round(eff, 4), cost_ms_median=round(med, 4),
+                cost_ms_q1=round(q_(diffs, 0.25), 4), cost_ms_q3=round(q_(diffs, 0.75), 4),
+                cost_ms_min=round(diffs[0], 4), cost_ms_max=round(diffs[-1], 4),
+                cost_frac_of_ring=round(med / q_(sorted(tr), 0.5), 6),
+                t_ring_ms=round(q_(sorted(tr), 0.5), 4), t_nocopy_ms=round(q_(sorted(tn), 0.5), 4),
+                t_copy_ms=round(t_copy, 4), reps=reps,
                 copy_bytes=int(2 * (n - 1) * w["k"][0].numel() * w["k"].element_size()))
 
 
@@ -262,9 +279,11 @@ def merge_leg(w, reps=5):
                 frac_of_peak=round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4))
 
 
-def cpu_baseline_leg(w, n_rows, k_global, v_global):
+def cpu_baseline_leg(w, n_rows, k_global, v_global, gpu_out=None):
     """The fp64 oracle (untuned) on n_rows sampled query rows x all heads of
-    the share; rate in counted TFLOP/s of those rows."""
+    the share; rate in counted TFLOP/s of those rows. With gpu_out (the
+    ring's output of the same share), also the max-abs error of those rows
+    against the oracle."""
     from oracle import ring_oracle as orc
     c = w["cfg"]
     rows = workloads.sample_rows(c["block"], n_rows, seed=3)
@@ -274,8 +293,18 @@ def cpu_baseline_leg(w, n_rows, k_global, v_global):
     k64 = k_global[:, :kmax].to(torch.float64).cpu().numpy()
     v64 = v_global[:, :kmax].to(torch.float64).cpu().numpy()
     t0 = time.perf_counter()
-    orc.naive_attention_rows(q_rows, tok.numpy(), k64, v64, c["causal"])
+    ref, ref_lse = orc.naive_attention_rows(q_rows, tok.numpy(), k64, v64, c["causal"])
     dt = time.perf_counter() - t0
+    parity = None
+    if gpu_out is not None:
+        got_o, got_l = gpu_out
+        d_o = (got_o[:, rows.to(got_o.device)].to(torch.float64).cpu().numpy() - ref)
+        d_l = (got_l[:, rows.to(got_l.device)].to(torch.float64).cpu().numpy() - ref_lse)
+        parity = dict(max_abs=float(abs(d_o).max()), lse_max_abs=float(abs(d_l).max()),
+                      tol=1e-2, rows=len(tok), heads=c["hq"],
+                      reference="oracle O1 (fp64 softmax(QK^T/sqrt(d))V), every visible key",
+                      rows_sample="first/last 8, tile edges, seeded random rows",
+                      layout=w["layout"], rank=w["rank"])
     pairs = int((tok + 1).sum()) if c["causal"] else len(tok) * k_global.shape[1]
     flops = 4.0 * c["d"] * c["hq"] * pairs
     try:
@@ -287,7 +316,7 @@ def cpu_baseline_leg(w, n_rows, k_global, v_global):
                 kind="oracle",
                 sample=(f"{len(tok)} query rows x {c['hq']} heads of the {w['layout']} rank-{w['rank']}"
                         f" share, all visible keys, fp64 NumPy; {dt:.1f} s"),
-                seconds=round(dt, 2), host_cpus=len(os.sched_getaffinity(0)))
+                seconds=round(dt, 2), host_cpus=len(os.sched_getaffinity(0))), parity
 
 
 def setup_ring(w, dev):
@@ -332,6 +361,56 @@ def widened_leg(dev, cases, reps=2):
         del w
         torch.cuda.empty_cache()
         log(f"[bench] widened {key} done")
+    return res
+
+
+def configs_leg(dev, reps=3):
+    """Ring TF/s of the other bf16 workloads, each ring as the library runs it
+    by default (one warm-up, median of `reps`): the 8192-token causal
+    sequence (every rank's share, times summed), the 131072-token striped GQA
+    share at every rank r = 0..7 (r = 7 is the headline rank; the sweep shows
+    the load of the early-query devices), and the non-causal 921,600-token
+    video share (rank 0; all ranks do equal work)."""
+    res = {}
+
+    def ring_ms(w):
+        ring_call(w, w["out"], w["lse"], w["ws"])
+        torch.cuda.synchronize()
+        ts = sorted(timed(lambda: ring_call(w, w["out"], w["lse"], w["ws"])) for _ in range(reps))
+        return ts[len(ts) // 2]
+
+    def entry(ms, flops):
+        tf = flops / (ms / 1e3) / 1e12
+        return dict(ms=round(ms, 4), tflops=round(tf, 2),
+                    pct_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), counted_flops=flops)
+
+    tot_ms = tot_f = 0.0
+    for r in range(8):
+        w = workloads.prepare("c2", "contiguous", r, device=dev)
+        setup_ring(w, dev)
+        tot_ms += ring_ms(w)
+        tot_f += w["flops"]
+        del w
+    res["c2"] = dict(workload="8192 tokens, N=8 blocks of 1024, 32 heads, causal contiguous, "
+                              "every rank (ring times summed)", **entry(tot_ms, tot_f))
+    log("[bench] configs c2 done")
+    sweep = {}
+    for r in range(8):
+        w = workloads.prepare("c3", "striped", r, device=dev)
+        setup_ring(w, dev)
+        sweep[str(r)] = entry(ring_ms(w), w["flops"])
+        del w
+    torch.cuda.empty_cache()
+    res["c3"] = dict(workload="131072 tokens, N=8 blocks of 16384, GQA 32/8, causal striped",
+                     rank7=sweep["7"], rank_sweep=sweep)
+    log("[bench] configs c3 done")
+    w = workloads.prepare("c5", "contiguous", 0, device=dev)
+    setup_ring(w, dev)
+    res["c5"] = dict(workload="921,600 tokens (3600 frames x 256), N=8 blocks of 115200, 32 heads, "
+                              "non-causal, rank 0", **entry(ring_ms(w), w["flops"]))
+    del w
+    torch.cuda.empty_cache()
+    log("[bench] configs c5 done")
     return res
 
 
@@ -415,6 +494,11 @@ def main():
     ap.add_argument("--skip-backward", action="store_true", help="no backward leg")
     ap.add_argument("--backward-only", action="store_true",
                     help="only the backward leg (kernel-trace runs of the backward kernels)")
+    ap.add_argument("--overlap-reps", type=int, default=11,
+                    help="interleaved (ring, no-copy) pairs per layout in the overlap leg")
+    ap.add_argument("--overlap-only", action="store_true",
+                    help="only the overlap leg of the workload's layouts (kernel-trace runs of "
+                         "the staged ring against the no-copy sequence)")
     ap.add_argument("--skip-aux", action="store_true",
                     help="no 8192-token overlap and no widened leg, so that every attention "
                          "launch has the headline workload's shape (kernel-trace runs)")
@@ -448,6 +532,16 @@ def main():
         ws_list.append(w)
         torch.cuda.synchronize()
         log(f"[bench] prepared {layout} in {time.time() - t0:.1f}s")
+
+    if args.overlap_only:
+        ov = {}
+        for w in ws_list:
+            ring_call(w, w["out"], w["lse"], w["ws"])
+            torch.cuda.synchronize()
+            ov[w["layout"]] = overlap_leg(w, w["out"], w["lse"], w["ws"], reps=args.overlap_reps)
+            log(f"[bench] overlap {w['layout']} done")
+        print(json.dumps({"overlap": ov}), flush=True)
+        return
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -544,32 +638,38 @@ def main():
         log("[bench] kernel leg done")
         # every layout, so that the attention launches of the whole run have the
         # same mix as the kernel leg (its average is compared with rocprofv3's)
-        ov = {w["layout"]: overlap_leg(w, w["out"], w["lse"], w["ws"]) for w in ws_list}
-        tot = {k: sum(o[k] for o in ov.values()) for k in ("t_ring_ms", "t_nocopy_ms", "t_copy_ms")}
-        eff = 1.0 - max(0.0, tot["t_ring_ms"] - tot["t_nocopy_ms"]) / tot["t_copy_ms"]
-        # On the 1M-token share the copies (~3 ms) are below the run-to-run
-        # spread of a ~3 s ring, so this timing difference is noise; the
-        # kernel trace (profiling.py trace) measures that case directly. The
-        # same timing method is resolved on the 8192-token workload, whose
-        # steps are tens of microseconds and whose copies are a visible share.
-        result["overlap"] = dict(efficiency_timing=round(eff, 4),
-                                 **{k: round(v, 3) for k, v in tot.items()}, per_layout=ov,
-                                 note="timing difference below run-to-run spread; see "
-                                      "small_workload and the kernel-trace figure")
+        ov = {}
+        for w in ws_list:
+            ov[w["layout"]] = overlap_leg(w, w["out"], w["lse"], w["ws"], reps=args.overlap_reps)
+            log(f"[bench] overlap {w['layout']} done")
+        tot = {k: sum(o[k] for o in ov.values())
+               for k in ("t_ring_ms", "t_nocopy_ms", "t_copy_ms", "cost_ms_median")}
+        eff = 1.0 - max(0.0, tot["cost_ms_median"]) / tot["t_copy_ms"]
+        result["overlap"] = dict(
+            efficiency=round(eff, 4), **{k: round(v, 4) for k, v in tot.items()},
+            per_layout=ov,
+            note=("cost = median over interleaved (ring, no-copy) pairs of T_ring - T_nocopy; "
+                  "efficiency = 1 - max(0, cost) / T_copy; quartiles and range per layout"))
         if args.workload != "c2" and not args.skip_aux:
             w2 = workloads.prepare("c2", "contiguous", 7, device=dev)
-            b2, lq2, hq2, d2 = w2["q"].shape
-            prob2 = B.make_problem(dtype=w2["q"].dtype, batch=b2, hq=hq2, hkv=w2["k"].shape[3],
-                                   head_dim=d2, q_len=lq2, kv_len=w2["k"].shape[2], n_ring=8,
-                                   rank=7, causal=True, layout="contiguous")
-            out2 = torch.empty(b2, lq2, hq2, d2, dtype=torch.float32, device=dev)
-            lse2 = torch.empty(b2, lq2, hq2, dtype=torch.float32, device=dev)
-            ws2 = torch.empty(B.ra_ring_workspace_bytes(prob2), dtype=torch.uint8, device=dev)
+            setup_ring(w2, dev)
+            out2, lse2, ws2 = w2["out"], w2["lse"], w2["ws"]
             ring_call(w2, out2, lse2, ws2)
-            result["overlap"]["small_workload"] = dict(
-                workload="c2: 8192 tokens, N=8 blocks of 1024, causal contiguous, rank 7",
-                **overlap_leg(w2, out2, lse2, ws2, reps=41),
-                graph=overlap_leg(w2, out2, lse2, ws2, reps=41, graph=True))
+            small = dict(workload="c2: 8192 tokens, N=8 blocks of 1024, causal contiguous, rank 7",
+                         default=overlap_leg(w2, out2, lse2, ws2, reps=41),
+                         graph=overlap_leg(w2, out2, lse2, ws2, reps=41, graph=True))
+            # the two-stream scheme forced at this size (the library would run
+            # copies this small in order on the compute stream)
+            prev = os.environ.get("RA_SIDE_STREAM_MIN_BYTES")
+            os.environ["RA_SIDE_STREAM_MIN_BYTES"] = "0"
+            try:
+                small["side_stream_forced"] = overlap_leg(w2, out2, lse2, ws2, reps=41)
+            finally:
+                if prev is None:
+                    os.environ.pop("RA_SIDE_STREAM_MIN_BYTES", None)
+                else:
+                    os.environ["RA_SIDE_STREAM_MIN_BYTES"] = prev
+            result["overlap"]["small_workload"] = small
             del w2, out2, lse2, ws2
         log("[bench] overlap leg done")
         result["merge"] = merge_leg(ws_list[0])
@@ -586,11 +686,15 @@ def main():
                       "part of value"),
                 **widened_leg(dev, [("c4", "zigzag", 0.0), ("c4p", "zigzag", 0.0),
                                     ("c4p", "contiguous", 0.0), ("c4", "zigzag", 500000.0)]))
+            result["configs"] = configs_leg(dev)
 
     if not args.skip_cpu and ws_list[0].get("cu_seqlens") is None:
         w = ws_list[0]
+        ring_call(w, w["out"], w["lse"], w["ws"])   # the ring's own output of this share
+        torch.cuda.synchronize()
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows ...")
-        result["cpu_baseline"] = cpu_baseline_leg(w, args.cpu_rows, w["k_global"], w["v_global"])
+        result["cpu_baseline"], result["parity"] = cpu_baseline_leg(
+            w, args.cpu_rows, w["k_global"], w["v_global"], gpu_out=(w["out"], w["lse"]))
         log("[bench] cpu baseline done")
 
     print(json.dumps(result), flush=True)

@@ -190,7 +190,12 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob);
  * staged and rotated on the way (V is copied as is).
  * Blocks whose every pair is masked are still staged but not computed.
  * copy_stream may be NULL or equal to compute_stream: copies then run in
- * order on compute_stream. On return all work is enqueued; everything
+ * order on compute_stream. They also run in order there when one step's
+ * copy (its K and V block) is under 32 MiB: a second stream costs each step
+ * two cross-stream waits on the critical path (about 10 us on MI355X),
+ * more than copies that small take (environment RA_SIDE_STREAM_MIN_BYTES
+ * overrides the size; 0 always uses copy_stream). The results are the same
+ * bits either way. On return all work is enqueued; everything
  * enqueued on copy_stream is ordered before the last kernel on
  * compute_stream, so synchronising compute_stream is enough.
  * Calls on the same device are serialised internally while enqueuing;

@@ -117,10 +117,41 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(None if t is None else t.data_ptr())
 
 
-def _stream(s, device) -> ctypes.c_void_p:
-    if s is None:
-        s = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+class _OnStream:
+    """Orders a library call on stream `s` (None: the current stream) after
+    the current stream, and keeps the tensors this binding allocated for the
+    call reserved for `s` and `extra` streams.
+
+    The binding allocates outputs (and zero-fills accumulated ones) on the
+    current stream. When the call runs elsewhere, `s` first waits for the
+    current stream, so those fills land before the library writes or adds
+    into the tensors; and each allocated tensor is recorded on `s` (and on a
+    side copy stream), so the caching allocator does not hand its memory to
+    later work on the current stream while `s` may still use it."""
+
+    def __init__(self, s, device, extra=()):
+        cur = torch.cuda.current_stream(device)
+        self.stream = cur if s is None else s
+        self.other = self.stream != cur
+        if self.other:
+            self.stream.wait_stream(cur)
+        self.extra = [x for x in extra if isinstance(x, torch.cuda.Stream) and x != cur]
+        self.owned = []
+
+    def own(self, t):
+        if t is not None:
+            self.owned.append(t)
+        return t
+
+    def handle(self) -> ctypes.c_void_p:
+        return ctypes.c_void_p(self.stream.cuda_stream)
+
+    def done(self):
+        targets = ([self.stream] if self.other else []) + [x for x in self.extra
+                                                            if x != self.stream]
+        for t in self.owned:
+            for st in targets:
+                t.record_stream(st)
 
 
 def make_problem(*, dtype, batch, hq, hkv, head_dim, q_len, kv_len, n_ring, rank, causal,
@@ -180,16 +211,18 @@ def ra_block_attn_partial(q, k, v, kv_block_j: int, *, n_ring: int, rank: int, c
     b, lq, hq, d = q.shape
     _need(k, "k", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
     _need(v, "v", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
-    m = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device) if m is None else m
-    l = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device) if l is None else l
-    acc = torch.empty(b, lq, hq, d, dtype=torch.float32, device=q.device) if acc is None else acc
-    _need(m, "m", torch.float32, (b, lq, hq), q.device)
-    _need(l, "l", torch.float32, (b, lq, hq), q.device)
-    _need(acc, "acc", torch.float32, (b, lq, hq, d), q.device)
     with torch.cuda.device(q.device):
+        on = _OnStream(stream, q.device)
+        m = on.own(torch.empty(b, lq, hq, dtype=torch.float32, device=q.device)) if m is None else m
+        l = on.own(torch.empty(b, lq, hq, dtype=torch.float32, device=q.device)) if l is None else l
+        acc = on.own(torch.empty(b, lq, hq, d, dtype=torch.float32, device=q.device)) \
+            if acc is None else acc
+        _need(m, "m", torch.float32, (b, lq, hq), q.device)
+        _need(l, "l", torch.float32, (b, lq, hq), q.device)
+        _need(acc, "acc", torch.float32, (b, lq, hq, d), q.device)
         _check(lib().ra_block_attn_partial(ctypes.byref(prob), int(kv_block_j), _ptr(q), _ptr(k),
-                                           _ptr(v), _ptr(m), _ptr(l), _ptr(acc),
-                                           _stream(stream, q.device)))
+                                           _ptr(v), _ptr(m), _ptr(l), _ptr(acc), on.handle()))
+        on.done()
     return m, l, acc
 
 
@@ -204,16 +237,19 @@ def ra_merge_partials(m1, l1, acc1, m2, l2, acc2, *, out=None, stream=None):
         if t.numel() != rows:
             raise ValueError(f"{name} has {t.numel()} elements, expected {rows}")
     _need(acc2, "acc2", torch.float32, acc1.shape, dev)
-    if out is None:
-        out = (torch.empty_like(m1), torch.empty_like(l1), torch.empty_like(acc1))
-    mo, lo, ao = out
-    _need(mo, "m_out", torch.float32, m1.shape, dev)
-    _need(lo, "l_out", torch.float32, l1.shape, dev)
-    _need(ao, "acc_out", torch.float32, acc1.shape, dev)
     with torch.cuda.device(dev):
+        on = _OnStream(stream, dev)
+        if out is None:
+            out = (on.own(torch.empty_like(m1)), on.own(torch.empty_like(l1)),
+                   on.own(torch.empty_like(acc1)))
+        mo, lo, ao = out
+        _need(mo, "m_out", torch.float32, m1.shape, dev)
+        _need(lo, "l_out", torch.float32, l1.shape, dev)
+        _need(ao, "acc_out", torch.float32, acc1.shape, dev)
         _check(lib().ra_merge_partials(rows, d, _ptr(m1), _ptr(l1), _ptr(acc1), _ptr(m2),
                                        _ptr(l2), _ptr(acc2), _ptr(mo), _ptr(lo), _ptr(ao),
-                                       _stream(stream, dev)))
+                                       on.handle()))
+        on.done()
     return mo, lo, ao
 
 
@@ -225,11 +261,12 @@ def ra_finalize(m, l, acc, *, lse=None, want_lse=True, stream=None):
     dev = acc.device
     _need(m, "m", torch.float32, device=dev)
     _need(l, "l", torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty_like(m)
     with torch.cuda.device(dev):
-        _check(lib().ra_finalize(rows, d, _ptr(m), _ptr(l), _ptr(acc), _ptr(lse),
-                                 _stream(stream, dev)))
+        on = _OnStream(stream, dev)
+        if lse is None and want_lse:
+            lse = on.own(torch.empty_like(m))
+        _check(lib().ra_finalize(rows, d, _ptr(m), _ptr(l), _ptr(acc), _ptr(lse), on.handle()))
+        on.done()
     return acc, lse
 
 
@@ -256,30 +293,28 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
     dev = q.device
     _need(k, "k", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
     _need(v, "v", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
-    out = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev) if out is None else out
-    _need(out, "out", torch.float32, (b, lq, hq, d), dev)
-    if lse is None and want_lse:
-        lse = torch.empty(b, lq, hq, dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", torch.float32, (b, lq, hq), dev)
     need = ra_ring_workspace_bytes(prob)
     if need == 0 and b * lq * hq > 0:
         _check(lib().ra_ring_fwd(ctypes.byref(prob), None, None, None, None, None, None, 0,
                                  None, None))
-    own_ws = workspace is None
-    if own_ws:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        cs = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
         if copy_stream == "auto":
             copy_stream = side_stream(dev)
+        on = _OnStream(compute_stream, dev, extra=(copy_stream,))
+        out = on.own(torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev)) \
+            if out is None else out
+        _need(out, "out", torch.float32, (b, lq, hq, d), dev)
+        if lse is None and want_lse:
+            lse = on.own(torch.empty(b, lq, hq, dtype=torch.float32, device=dev))
+        if lse is not None:
+            _need(lse, "lse", torch.float32, (b, lq, hq), dev)
+        if workspace is None:
+            workspace = on.own(torch.empty(max(need, 1), dtype=torch.uint8, device=dev))
+        _need(workspace, "workspace", torch.uint8, device=dev)
         xs = ctypes.c_void_p(None) if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
         _check(lib().ra_ring_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                 _ptr(lse), _ptr(workspace), workspace.numel(),
-                                 ctypes.c_void_p(cs.cuda_stream), xs))
-        if own_ws:
-            _record(workspace, cs, copy_stream)
+                                 _ptr(lse), _ptr(workspace), workspace.numel(), on.handle(), xs))
+        on.done()
     return out, lse
 
 
@@ -291,12 +326,14 @@ def ra_attn_bwd_delta(out, dout, *, delta=None, stream=None):
         raise ValueError(f"unsupported dtype {dout.dtype}")
     d = out.shape[-1]
     rows = out.numel() // d if d else 0
-    if delta is None:
-        delta = torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device)
-    _need(delta, "delta", torch.float32, out.shape[:-1], out.device)
     with torch.cuda.device(out.device):
+        on = _OnStream(stream, out.device)
+        if delta is None:
+            delta = on.own(torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device))
+        _need(delta, "delta", torch.float32, out.shape[:-1], out.device)
         _check(lib().ra_attn_bwd_delta(rows, d, _DTYPE[dout.dtype], _ptr(out), _ptr(dout),
-                                       _ptr(delta), _stream(stream, out.device)))
+                                       _ptr(delta), on.handle()))
+        on.done()
     return delta
 
 
@@ -315,16 +352,22 @@ def ra_block_attn_bwd(q, k, v, dout, lse, delta, kv_block_j: int, *, n_ring: int
     _need(dout, "dout", q.dtype, q.shape, dev)
     _need(lse, "lse", torch.float32, (b, lq, hq), dev)
     _need(delta, "delta", torch.float32, (b, lq, hq), dev)
-    dq = torch.zeros(b, lq, hq, d, dtype=torch.float32, device=dev) if dq is None else dq
-    dk = torch.zeros(kshape, dtype=torch.float32, device=dev) if dk is None else dk
-    dv = torch.zeros(kshape, dtype=torch.float32, device=dev) if dv is None else dv
-    _need(dq, "dq", torch.float32, (b, lq, hq, d), dev)
-    _need(dk, "dk", torch.float32, kshape, dev)
-    _need(dv, "dv", torch.float32, kshape, dev)
     with torch.cuda.device(dev):
+        new = [t is None for t in (dq, dk, dv)]
+        dq = torch.zeros(b, lq, hq, d, dtype=torch.float32, device=dev) if dq is None else dq
+        dk = torch.zeros(kshape, dtype=torch.float32, device=dev) if dk is None else dk
+        dv = torch.zeros(kshape, dtype=torch.float32, device=dev) if dv is None else dv
+        on = _OnStream(stream, dev)   # ordered after the zero fills just queued
+        for t, n in zip((dq, dk, dv), new):
+            if n:
+                on.own(t)
+        _need(dq, "dq", torch.float32, (b, lq, hq, d), dev)
+        _need(dk, "dk", torch.float32, kshape, dev)
+        _need(dv, "dv", torch.float32, kshape, dev)
         _check(lib().ra_block_attn_bwd(ctypes.byref(prob), int(kv_block_j), _ptr(q), _ptr(k),
                                        _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
-                                       _ptr(dk), _ptr(dv), _stream(stream, dev)))
+                                       _ptr(dk), _ptr(dv), on.handle()))
+        on.done()
     return dq, dk, dv
 
 
@@ -350,31 +393,34 @@ def ra_ring_bwd(q, k, v, out, dout, lse, *, n_ring: int, causal: bool, layout="c
     _need(out, "out", torch.float32, (b, lq, hq, d), dev)
     _need(dout, "dout", q.dtype, q.shape, dev)
     _need(lse, "lse", torch.float32, (b, lq, hq), dev)
-    dq = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev) if dq is None else dq
-    dk = torch.zeros(kshape, dtype=torch.float32, device=dev) if dk is None else dk
-    dv = torch.zeros(kshape, dtype=torch.float32, device=dev) if dv is None else dv
-    _need(dq, "dq", torch.float32, (b, lq, hq, d), dev)
-    _need(dk, "dk", torch.float32, kshape, dev)
-    _need(dv, "dv", torch.float32, kshape, dev)
     need = ra_ring_bwd_workspace_bytes(prob)
     if need == 0 and b * lq * hq > 0:
         _check(lib().ra_ring_bwd(ctypes.byref(prob), None, None, None, None, None, None, None,
                                  None, None, None, 0, None, None))
-    own_ws = workspace is None
-    if own_ws:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        cs = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
         if copy_stream == "auto":
             copy_stream = side_stream(dev)
+        new = [t is None for t in (dq, dk, dv, workspace)]
+        dq = torch.empty(b, lq, hq, d, dtype=torch.float32, device=dev) if dq is None else dq
+        dk = torch.zeros(kshape, dtype=torch.float32, device=dev) if dk is None else dk
+        dv = torch.zeros(kshape, dtype=torch.float32, device=dev) if dv is None else dv
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        # the ring adds into dk, dv on the compute stream: it waits for their
+        # zero fills on the current stream first
+        on = _OnStream(compute_stream, dev, extra=(copy_stream,))
+        for t, n in zip((dq, dk, dv, workspace), new):
+            if n:
+                on.own(t)
+        _need(dq, "dq", torch.float32, (b, lq, hq, d), dev)
+        _need(dk, "dk", torch.float32, kshape, dev)
+        _need(dv, "dv", torch.float32, kshape, dev)
+        _need(workspace, "workspace", torch.uint8, device=dev)
         xs = ctypes.c_void_p(None) if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
         _check(lib().ra_ring_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                  _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 _ptr(workspace), workspace.numel(),
-                                 ctypes.c_void_p(cs.cuda_stream), xs))
-        if own_ws:
-            _record(workspace, cs, copy_stream)
+                                 _ptr(workspace), workspace.numel(), on.handle(), xs))
+        on.done()
     return dq, dk, dv
 
 
@@ -386,30 +432,24 @@ def ra_rope_apply(x, prob: RaProblem, *, target="keys", block_j: int = 0, out=No
     if x.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {x.dtype}")
     out_dtype = out_dtype or x.dtype
-    if out is None:
-        out = torch.zeros(x.shape, dtype=out_dtype, device=x.device) if accumulate else \
-            torch.empty(x.shape, dtype=out_dtype, device=x.device)
-    _need(out, "out", out_dtype, x.shape, x.device)
     tgt = RA_ROPE_QUERIES if target == "queries" else RA_ROPE_KEYS
     with torch.cuda.device(x.device):
+        fresh = out is None
+        if fresh:
+            out = torch.zeros(x.shape, dtype=out_dtype, device=x.device) if accumulate else \
+                torch.empty(x.shape, dtype=out_dtype, device=x.device)
+        on = _OnStream(stream, x.device)
+        if fresh:
+            on.own(out)
+        _need(out, "out", out_dtype, x.shape, x.device)
         _check(lib().ra_rope_apply(ctypes.byref(prob), tgt, int(block_j), int(x.shape[2]),
                                    _DTYPE[x.dtype], _ptr(x), _DTYPE[out_dtype], _ptr(out),
-                                   int(bool(inverse)), int(bool(accumulate)),
-                                   _stream(stream, x.device)))
+                                   int(bool(inverse)), int(bool(accumulate)), on.handle()))
+        on.done()
     return out
 
 
 _side = {}
-
-
-def _record(t, *streams):
-    """Keep an internally allocated device buffer reserved until the work
-    enqueued on `streams` (the ring's compute and copy streams) has run: the
-    caching allocator otherwise only orders its reuse after the stream it was
-    allocated on (the current one)."""
-    for st in streams:
-        if isinstance(st, torch.cuda.Stream):
-            t.record_stream(st)
 
 
 def side_stream(device) -> torch.cuda.Stream:
@@ -443,8 +483,11 @@ def ra_tile_classes_device(prob: RaProblem, kv_block_j: int, tq: int, tk: int, d
     nqt, nkt = -(-prob.q_len // tq), -(-prob.kv_len // tk)
     out = torch.full((nqt, nkt), -1, dtype=torch.int8, device=device)
     with torch.cuda.device(out.device):
+        on = _OnStream(stream, out.device)   # after the fill just queued
+        on.own(out)
         _check(lib().ra_tile_classes_device(ctypes.byref(prob), int(kv_block_j), int(tq), int(tk),
-                                            _ptr(out), _stream(stream, out.device)))
+                                            _ptr(out), on.handle()))
+        on.done()
     return out
 
 

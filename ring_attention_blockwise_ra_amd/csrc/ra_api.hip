@@ -129,16 +129,52 @@ ra_status validate_problem(const ra_problem* p, Shape* s) {
     return fail(RA_ERR_INVALID_ARG, "(hq/hkv)*q_len exceeds 2^31-1");
   ra_status st = validate_packed(p, s);
   if (st != RA_OK) return st;
-  // grid: batch * hkv * (row tiles of >= 128 rows per segment) must fit in 2^31
-  const int64_t tiles = (group * p->q_len + 127) / 128 + s->seg.n;
-  if ((int64_t)p->batch * p->hkv * tiles > INT32_MAX)
-    return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
   s->rows = (int64_t)p->batch * p->q_len * p->hq;
   s->q_elems = s->rows * p->head_dim;
   s->kv_elems = (int64_t)p->batch * p->kv_len * p->hkv * p->head_dim;
   s->elem = p->dtype == RA_BF16 ? 2 : 4;
   s->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   return RA_OK;
+}
+
+// Workgroups of one tiled launch for one (batch row, KV head), counted as
+// the launchers count them: row (or key) tiles of every segment.
+int64_t tiles_per_head(const ra_problem* p, const Shape& s, ra::TileShape t) {
+  int64_t total = 0;
+  const int64_t group = p->hq / p->hkv;
+  for (int i = 0; i < s.seg.n; ++i) {
+    const int64_t len = (int64_t)s.seg.off[i + 1] - s.seg.off[i];
+    const int64_t n = t.by_keys ? (s.packed ? len : (i == 0 ? p->kv_len : 0)) : len * group;
+    total += (n + t.per - 1) / t.per;
+  }
+  return total;
+}
+
+// One launch of `t` over the problem must fit a dispatch: at most 2^31 - 1
+// workgroups and 2^32 - 1 work items.
+ra_status check_grid(const ra_problem* p, const Shape& s, ra::TileShape t, const char* kernel) {
+  const int64_t heads = (int64_t)p->batch * p->hkv;
+  int64_t blocks = 0, items = 0;
+  if (__builtin_mul_overflow(heads, tiles_per_head(p, s, t), &blocks) || blocks > INT32_MAX ||
+      __builtin_mul_overflow(blocks, (int64_t)t.threads, &items) || items > (int64_t)0xFFFFFFFF)
+    return fail(RA_ERR_INVALID_ARG,
+                "problem too large for one launch of the %s kernel (%d %s and %d work items per "
+                "workgroup)", kernel, t.per, t.by_keys ? "keys" : "rows", t.threads);
+  return RA_OK;
+}
+
+int env_waves();
+
+ra_status check_fwd_grid(const ra_problem* p, const Shape& s) {
+  return check_grid(p, s, ra::fwd_tile_shape(p->dtype == RA_BF16, p->head_dim, env_waves()),
+                    "attention");
+}
+
+ra_status check_bwd_grid(const ra_problem* p, const Shape& s) {
+  ra::TileShape t[2];
+  ra::bwd_tile_shapes(p->dtype == RA_BF16, p->head_dim, t);
+  ra_status st = check_grid(p, s, t[0], "dq");
+  return st != RA_OK ? st : check_grid(p, s, t[1], "dk/dv");
 }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -152,6 +188,19 @@ ra_status check_ptr(const void* p, size_t bytes, const char* name) {
   if (p == nullptr) return fail(RA_ERR_INVALID_ARG, "%s is NULL", name);
   if (!aligned16(p)) return fail(RA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
   return RA_OK;
+}
+
+// Staging copies of fewer bytes per step than this (K and V of one block)
+// run in order on the compute stream even when a copy stream is given. A
+// second stream costs each step two cross-stream event waits that the GPU
+// resolves on the critical path (about 10 us per step measured on MI355X);
+// below this size the copies they would hide take less than that.
+// RA_SIDE_STREAM_MIN_BYTES overrides it (0: always use the copy stream); it
+// is read at every ring call.
+size_t side_stream_min_bytes() {
+  const char* e = getenv("RA_SIDE_STREAM_MIN_BYTES");
+  if (e && *e) return (size_t)strtoull(e, nullptr, 10);
+  return size_t(32) << 20;
 }
 
 // Waves per workgroup of the bf16 kernel: 8 (two per SIMD) unless RA_WAVES=4.
@@ -477,6 +526,7 @@ ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j, cons
     if (kv_block_j < 0 || kv_block_j >= prob->n_ring)
       return fail(RA_ERR_INVALID_ARG, "kv_block_j %d out of [0, n_ring=%d)", kv_block_j,
                   prob->n_ring);
+    if ((st = check_fwd_grid(prob, s)) != RA_OK) return st;
     const size_t qb = s.q_elems * s.elem, kb = s.kv_elems * s.elem;
     const size_t rb = s.rows * 4, ab = s.q_elems * 4;
     if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kb, "k")) ||
@@ -581,25 +631,36 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob) {
   }
 }
 
-ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, const void* v,
-                      float* out, float* lse, void* workspace, size_t workspace_bytes,
-                      void* compute_stream, void* copy_stream) {
+// The ring's tensors apart from the workspace: pointers, alignment, block
+// size (host-side only, before any HIP call).
+static ra_status check_ring_fwd_tensors(const ra_problem* prob, const Shape& s, const void* q,
+                                        const void* k, const void* v, const float* out,
+                                        const float* lse) {
+  ra_status st;
+  const size_t blk = s.kv_elems * s.elem, kvb = blk * prob->n_ring;
+  const size_t rb = s.rows * 4;
+  if ((st = check_ptr(q, s.q_elems * s.elem, "q")) || (st = check_ptr(k, kvb, "k")) ||
+      (st = check_ptr(v, kvb, "v")) || (st = check_ptr(out, s.q_elems * 4, "out")))
+    return st;
+  if (lse != nullptr && (st = check_ptr(lse, rb, "lse"))) return st;
+  if (blk % 16 != 0 && prob->n_ring > 1)
+    return fail(RA_ERR_INVALID_ARG, "one KV block (%zu bytes) must be a multiple of 16 bytes",
+                blk);
+  return RA_OK;
+}
+
+static ra_status ring_fwd_impl(const ra_problem* prob, const Shape& s, const void* q,
+                               const void* k, const void* v, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* compute_stream,
+                               void* copy_stream) {
   try {
-    Shape s;
-    ra_status st = validate_problem(prob, &s);
-    if (st != RA_OK) return st;
+    ra_status st;
     const int n = prob->n_ring;
     const size_t qb = s.q_elems * s.elem;
     const size_t blk = s.kv_elems * s.elem;
     const size_t kvb = blk * n;
     const size_t ob = s.q_elems * 4, rb = s.rows * 4;
-    if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kvb, "k")) ||
-        (st = check_ptr(v, kvb, "v")) || (st = check_ptr(out, ob, "out")))
-      return st;
-    if (lse != nullptr && (st = check_ptr(lse, rb, "lse"))) return st;
-    if (blk % 16 != 0 && n > 1)
-      return fail(RA_ERR_INVALID_ARG, "one KV block (%zu bytes) must be a multiple of 16 bytes",
-                  blk);
+    if ((st = check_ring_fwd_tensors(prob, s, q, k, v, out, lse)) != RA_OK) return st;
     const WsLayout w = ws_layout(prob, s);
     if (s.rows > 0) {
       if (workspace == nullptr || workspace_bytes < w.total)
@@ -627,7 +688,7 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
     // ---- enqueue -------------------------------------------------------
     hipStream_t cs = static_cast<hipStream_t>(compute_stream);
     hipStream_t xs = static_cast<hipStream_t>(copy_stream);
-    const bool sep = xs != nullptr && xs != cs;
+    const bool sep = xs != nullptr && xs != cs && 2 * blk >= side_stream_min_bytes();
     DeviceEvents* de = nullptr;
     if ((st = get_events(&de)) != RA_OK) return st;
     std::lock_guard<std::mutex> lk(de->mu);
@@ -677,6 +738,21 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
   }
 }
 
+ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, const void* v,
+                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    if ((st = check_fwd_grid(prob, s)) != RA_OK) return st;
+    return ring_fwd_impl(prob, s, q, k, v, out, lse, workspace, workspace_bytes, compute_stream,
+                         copy_stream);
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const float* out,
                             const void* dout, float* delta, void* hip_stream) {
   try {
@@ -716,6 +792,7 @@ ra_status ra_block_attn_bwd(const ra_problem* prob, int32_t kv_block_j, const vo
     if (kv_block_j < 0 || kv_block_j >= prob->n_ring)
       return fail(RA_ERR_INVALID_ARG, "kv_block_j %d out of [0, n_ring=%d)", kv_block_j,
                   prob->n_ring);
+    if ((st = check_bwd_grid(prob, s)) != RA_OK) return st;
     const size_t qb = s.q_elems * s.elem, kb = s.kv_elems * s.elem;
     const size_t rb = s.rows * 4, qfb = s.q_elems * 4, kfb = s.kv_elems * 4;
     if ((st = check_ptr(q, qb, "q")) || (st = check_ptr(k, kb, "k")) ||
@@ -762,6 +839,7 @@ ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, cons
     Shape s;
     ra_status st = validate_problem(prob, &s);
     if (st != RA_OK) return st;
+    if ((st = check_bwd_grid(prob, s)) != RA_OK) return st;
     const int n = prob->n_ring;
     const size_t qb = s.q_elems * s.elem, blk = s.kv_elems * s.elem, kvb = blk * n;
     const size_t qfb = s.q_elems * 4, rb = s.rows * 4, kfb = s.kv_elems * 4 * n;
@@ -798,7 +876,7 @@ ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, cons
 
     hipStream_t cs = static_cast<hipStream_t>(compute_stream);
     hipStream_t xs = static_cast<hipStream_t>(copy_stream);
-    const bool sep = xs != nullptr && xs != cs;
+    const bool sep = xs != nullptr && xs != cs && 2 * blk >= side_stream_min_bytes();
     DeviceEvents* de = nullptr;
     if ((st = get_events(&de)) != RA_OK) return st;
     std::lock_guard<std::mutex> lk(de->mu);

@@ -978,6 +978,18 @@ static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+void bwd_tile_shapes(int is_bf16, int head_dim, TileShape out[2]) {
+  if (is_bf16) {
+    out[0] = TileShape{32 * kDqWaves, 64 * kDqWaves, 0};
+    out[1] = TileShape{32 * kKvWaves, 64 * kKvWaves, 1};
+    return;
+  }
+  const int dc = head_dim < 32 ? head_dim : 32;
+  const int per = kThreads / (head_dim / dc);
+  out[0] = TileShape{per, kThreads, 0};
+  out[1] = TileShape{per, kThreads, 1};
+}
+
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t stream) {
   if (is_bf16) {
     switch (p.head_dim) {

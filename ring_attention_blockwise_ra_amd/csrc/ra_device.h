@@ -34,7 +34,9 @@ constexpr int kThreads = 256;  // workgroup size of the fp32 and elementwise ker
 // grid-stride but are launched with one workgroup per kThreads work items up
 // to this many: a grid covering the whole array keeps far more loads in
 // flight than a smaller grid looping over it (merge 4.5 -> 5.9 TB/s).
-constexpr int64_t kMaxGridBlocks = int64_t(1) << 24;
+// The dispatch packet counts work items in 32 bits, so a grid holds at most
+// 2^32 - 1 of them.
+constexpr int64_t kMaxGridBlocks = int64_t(0xFFFFFFFF) / kThreads;
 constexpr int kTK = 64;        // keys per tile
 constexpr int kSlots = 4;      // LDS ring of K/V tiles; loads run kSlots-1 tiles ahead
 

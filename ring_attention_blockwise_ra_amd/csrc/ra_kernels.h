@@ -103,6 +103,20 @@ hipError_t allow_dynamic_lds(const void* kern, size_t bytes);
 // waves: wavefronts per workgroup of the bf16 kernel (4 or 8; 32 rows each).
 hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream);
 
+// How a tiled kernel covers one (batch row, KV head): `per` query rows (the
+// rows a*G + hh of the G grouped heads) or, with by_keys, `per` keys of the
+// block per workgroup, with `threads` work items per workgroup; a packed
+// share adds one partial tile per segment. The launchers tile with these
+// numbers and the C ABI validates every launch's grid against them.
+struct TileShape {
+  int per;
+  int threads;
+  int by_keys;
+};
+TileShape fwd_tile_shape(int is_bf16, int head_dim, int waves);
+// the backward's two launches: dq over query rows, then dk/dv over keys
+void bwd_tile_shapes(int is_bf16, int head_dim, TileShape out[2]);
+
 hipError_t launch_merge(int64_t rows, int d, const float* m1, const float* l1, const float* a1,
                         const float* m2, const float* l2, const float* a2, float* mo, float* lo,
                         float* ao, hipStream_t stream);

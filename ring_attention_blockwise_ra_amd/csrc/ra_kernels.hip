@@ -667,6 +667,12 @@ static hipError_t launch_f32(AttnParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+TileShape fwd_tile_shape(int is_bf16, int head_dim, int waves) {
+  if (is_bf16) return TileShape{32 * waves, 64 * waves, 0};
+  const int dc = head_dim < 32 ? head_dim : 32;  // attn_f32_fma: one thread per (row, 32 dims)
+  return TileShape{kThreads / (head_dim / dc), kThreads, 0};
+}
+
 hipError_t launch_attention(const AttnParams& p, int is_bf16, int waves, hipStream_t stream) {
   if (is_bf16) {
     if (waves == 4) {

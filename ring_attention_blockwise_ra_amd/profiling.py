@@ -1,8 +1,9 @@
 """Summaries of rocprofv3 output for the attention path.
 
-    python -m ring_attention_blockwise_ra_amd.profiling trace  <kernel_trace.csv> <kernel_stats.csv>
+    python -m ring_attention_blockwise_ra_amd.profiling trace  <kernel_trace.csv> <kernel_stats.csv> [ms_per_step launches_per_step]
     python -m ring_attention_blockwise_ra_amd.profiling traffic <fetch_dir> <write_dir> <out.json>
     python -m ring_attention_blockwise_ra_amd.profiling sq <pmc_dir> [kernel name part]
+    python -m ring_attention_blockwise_ra_amd.profiling overlap <kernel_trace.csv> <launches per ring>
 
 trace:   per-kernel statistics of the attention, merge and finalize kernels,
          and how much of the side-queue staging copy time ran while an
@@ -12,6 +13,9 @@ traffic: HBM bytes per attention launch from two counter runs (FETCH_SIZE,
          counter reads for the calibration copy of known size that bench.py
          performs with --calib-copy-mib. Writes a JSON that bench.py reports
          as roofline.traffic while the kernel source hash still matches.
+overlap: attention-kernel time of each staged ring against each no-copy
+         sequence in a trace of bench.py --overlap-only (what concurrent
+         staging copies cost the kernels).
 sq:      shader-sequencer counters of the attention launches (one --pmc run
          with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU,
          SQ_INSTS_VALU_TRANS_F32, SQ_INSTS_LDS, GRBM_GUI_ACTIVE and others):
@@ -51,7 +55,12 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def trace_summary(trace_csv: str, stats_csv: str) -> dict:
+def trace_summary(trace_csv: str, stats_csv: str, ms_per_step: float | None = None,
+                  launches_per_step: int | None = None) -> dict:
+    """With ms_per_step (bench's figure of the same run) and the attention
+    launches one step makes, also checks that the traced average launch time
+    fits the timed step: launches_per_step x average <= ms_per_step (a trace
+    taken on a slower box, or of other source, cannot stand for the run)."""
     rows = _rows(trace_csv)
     attn = [r for r in rows if ATTN in r["Kernel_Name"]]
     attn_q = {r["Queue_Id"] for r in attn}
@@ -73,9 +82,49 @@ def trace_summary(trace_csv: str, stats_csv: str) -> dict:
                 stats[name[:80]] = dict(calls=int(r["Calls"]), avg_ms=float(r["AverageNs"]) / 1e6,
                                         total_ms=float(r["TotalDurationNs"]) / 1e6,
                                         pct=float(r["Percentage"]))
-    return dict(kernels=stats, staging_copies=len(copies), staging_copy_ms=tot / 1e6,
-                staging_copy_hidden_ms=hidden / 1e6,
-                staging_copy_hidden_frac=(hidden / tot) if tot else None)
+    out = dict(kernels=stats, staging_copies=len(copies), staging_copy_ms=tot / 1e6,
+               staging_copy_hidden_ms=hidden / 1e6,
+               staging_copy_hidden_frac=(hidden / tot) if tot else None)
+    if ms_per_step is not None and launches_per_step:
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in attn]
+        avg = sum(durs) / len(durs)
+        out["attention_avg_ms"] = avg
+        out["attention_ms_per_step"] = launches_per_step * avg
+        out["ms_per_step"] = ms_per_step
+        if launches_per_step * avg > ms_per_step:
+            raise ValueError(f"{launches_per_step} launches x {avg:.3f} ms = "
+                             f"{launches_per_step * avg:.1f} ms exceed the step's {ms_per_step:.1f} ms")
+    return out
+
+
+def overlap_summary(trace_csv: str, launches: int) -> dict:
+    """Attention-kernel time of the staged ring against the no-copy sequence,
+    from a kernel trace of bench.py --overlap-only: attention dispatches in
+    start order, taken `launches` at a time (one ring, or one no-copy
+    sequence); a run is "staged" when staging copies ran on another queue
+    within its span. Returns the summed attention duration of each run, the
+    mean per kind, and the staged-minus-no-copy difference: what concurrent
+    copies cost the kernels themselves."""
+    rows = _rows(trace_csv)
+    attn = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Queue_Id"])
+                  for r in rows if ATTN in r["Kernel_Name"])
+    attn_q = {q for _, _, q in attn}
+    copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+              if COPY in r["Kernel_Name"] and r["Queue_Id"] not in attn_q]
+    runs = {"staged": [], "nocopy": []}
+    for i in range(0, len(attn) - launches + 1, launches):
+        grp = attn[i:i + launches]
+        a, b = grp[0][0], grp[-1][1]
+        staged = any(s < b and e > a for s, e in copies)
+        runs["staged" if staged else "nocopy"].append(sum(e - s for s, e, _ in grp) / 1e6)
+    mean = {k: (sum(v) / len(v) if v else None) for k, v in runs.items()}
+    diff = (mean["staged"] - mean["nocopy"]) if None not in mean.values() else None
+    return dict(launches_per_run=launches, runs={k: len(v) for k, v in runs.items()},
+                attention_ms_per_run=runs, mean_attention_ms=mean,
+                staged_minus_nocopy_ms=diff,
+                staged_minus_nocopy_frac=(diff / mean["nocopy"]) if diff is not None else None,
+                staging_copies=len(copies),
+                staging_copy_ms=sum(e - s for s, e in copies) / 1e6)
 
 
 def _counter_values(run_dir: str, counter: str):
@@ -174,7 +223,8 @@ def sq_summary(run_dir: str, kernel: str = ATTN) -> dict:
 
 def main(argv):
     if len(argv) >= 3 and argv[0] == "trace":
-        print(json.dumps(trace_summary(argv[1], argv[2]), indent=1))
+        extra = (float(argv[3]), int(argv[4])) if len(argv) >= 5 else (None, None)
+        print(json.dumps(trace_summary(argv[1], argv[2], *extra), indent=1))
     elif len(argv) >= 4 and argv[0] == "traffic":
         calib = int(argv[4]) if len(argv) > 4 else 1 << 30
         t = traffic(argv[1], argv[2], calib)
@@ -182,6 +232,8 @@ def main(argv):
         with open(argv[3], "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t, indent=1))
+    elif len(argv) >= 3 and argv[0] == "overlap":
+        print(json.dumps(overlap_summary(argv[1], int(argv[2])), indent=1))
     elif len(argv) >= 2 and argv[0] == "sq":
         print(json.dumps(sq_summary(argv[1], *argv[2:3]), indent=1))
     else:

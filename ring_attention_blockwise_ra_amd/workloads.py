@@ -77,16 +77,25 @@ def prepare(cfg_name: str, layout: str, rank: int, device="cuda", keep_global: b
     return out
 
 
-def sample_rows(block_len: int, n: int, seed: int = 0, tile_edges=(128, 256)) -> torch.Tensor:
-    """Local query rows to check at full size: the first 8, the last 8, rows on
-    both sides of tile edges, and seeded random rows, up to n in total."""
-    rows = set(range(min(8, block_len)))
-    rows |= set(range(max(0, block_len - 8), block_len))
+def sample_rows(block_len: int, n: int, seed: int = 0, tile_edges=(128, 256),
+                n_random: int | None = None) -> torch.Tensor:
+    """Local query rows to check at full size, at most n: the first 8 and the
+    last 8 rows, rows on both sides of tile edges (and of the block's
+    middle), then seeded random rows. At least n_random (default n // 2)
+    of the n are random rows, so every sample mixes edges with the interior;
+    when n is small the edge rows are kept in that order of priority."""
+    n = max(0, min(n, block_len))
+    n_random = n // 2 if n_random is None else min(n_random, n)
+    edges = []
+    for r in list(range(min(8, block_len))) + list(range(max(0, block_len - 8), block_len)):
+        if r not in edges:
+            edges.append(r)
     for t in tile_edges:
         for e in (t - 1, t, 2 * t - 1, 2 * t, block_len // 2 - 1, block_len // 2):
-            if 0 <= e < block_len:
-                rows.add(e)
+            if 0 <= e < block_len and e not in edges:
+                edges.append(e)
+    chosen = set(edges[:n - n_random])
     g = torch.Generator().manual_seed(seed)
-    while len(rows) < min(n, block_len):
-        rows.add(int(torch.randint(0, block_len, (1,), generator=g)))
-    return torch.tensor(sorted(rows)[:max(n, 0)], dtype=torch.int64)
+    while len(chosen) < n:
+        chosen.add(int(torch.randint(0, block_len, (1,), generator=g)))
+    return torch.tensor(sorted(chosen), dtype=torch.int64)

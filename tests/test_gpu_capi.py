@@ -18,7 +18,7 @@ from ring_attention_blockwise_ra_amd import build as BUILD
 from ring_attention_blockwise_ra_amd import synth
 from ring_attention_blockwise_ra_amd.layout import blocks_from_global, share_tokens
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always")]
 LAYOUT_ID = {"contiguous": 0, "striped": 1, "zigzag": 2}
 
 

@@ -18,7 +18,7 @@ from ring_attention_blockwise_ra_amd import binding as B
 from ring_attention_blockwise_ra_amd import synth, workloads
 from ring_attention_blockwise_ra_amd.layout import blocks_from_global, share_tokens
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always")]
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 DEV = "cuda"
@@ -242,6 +242,34 @@ def test_ring_on_a_side_compute_stream_keeps_its_own_workspace():
         assert torch.equal(out, ref)
 
 
+def test_ring_bwd_on_a_side_compute_stream_after_held_back_zero_fills():
+    """ra_ring_bwd on a compute stream that is not the current one, with dk
+    and dv allocated and zero-filled by the binding on the current stream,
+    which a spin holds back: the ring adds into dk, dv, so it must run after
+    those fills. Every gradient must equal the current-stream result."""
+    say("ring backward: zero fills on the held-back current stream, ring on a side stream")
+    n, blen, hq, hkv, d = 4, 256, 8, 2, 128
+    qg, kg, vg = _rand_global(8, 1, n * blen, hq, hkv, d, "bf16")
+    kb, vb = blocks_from_global(kg, "striped", n), blocks_from_global(vg, "striped", n)
+    r = 1
+    q = qg[:, share_tokens("striped", n, r, blen).to(DEV)].contiguous()
+    out, lse = B.ra_ring_fwd(q, kb, vb, n_ring=n, causal=True, layout="striped", rank=r)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    dout = torch.randn(q.shape, generator=g, device=DEV).to(torch.bfloat16)
+    ref = B.ra_ring_bwd(q, kb, vb, out, dout, lse, n_ring=n, causal=True, layout="striped", rank=r)
+    torch.cuda.synchronize()
+    assert float(ref[1].abs().max()) > 0 and float(ref[2].abs().max()) > 0
+    cs = torch.cuda.Stream()
+    for _ in range(3):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(2_000_000)   # on the current stream, before the fills
+        got = B.ra_ring_bwd(q, kb, vb, out, dout, lse, n_ring=n, causal=True, layout="striped",
+                            rank=r, compute_stream=cs)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(a, b), name
+
+
 # ---------------------------------------------------------------- invariants
 def test_causal_row0_and_constant_keys_on_gpu():
     say("invariants: row 0 = V[0]; constant keys = mean of visible V")
@@ -342,6 +370,11 @@ def test_tile_classes_device_match_host():
                     if blen <= 1000:
                         want = orc.tile_classes_bruteforce(layout, True, n, r, j, blen, blen, tq, tk)
                         np.testing.assert_array_equal(host, want)  # same integer codes
+                    else:  # the device form's class counts against the oracle's own counts
+                        cnt = np.bincount(dev.ravel().astype(np.int64), minlength=3)
+                        assert (int(cnt[B.RA_TILE_FULL]), int(cnt[B.RA_TILE_PARTIAL]),
+                                int(cnt[B.RA_TILE_SKIP])) == \
+                            orc.tile_class_counts(layout, True, n, r, j, blen, blen, tq, tk)
 
 
 def test_invalid_head_dim_raises():

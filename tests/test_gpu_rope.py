@@ -20,7 +20,7 @@ from ring_attention_blockwise_ra_amd import synth, workloads
 from ring_attention_blockwise_ra_amd.layout import (blocks_from_global, packed_blocks_from_global,
                                                     packed_share_tokens, share_tokens)
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always")]
 TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 DEV = "cuda"
 THETA = 10000.0

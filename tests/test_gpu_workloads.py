@@ -62,14 +62,15 @@ def _check_rows(out, w, rows, k_glob, v_glob, tol=1e-2, per_head=False):
         ref, _ = orc.naive_attention_rows(_f64(q_rows), tok, _f64(k_glob[:, :kmax]),
                                           _f64(v_glob[:, :kmax]), c["causal"])
         worst = float(np.abs(got - ref).max())
-    else:
+    else:  # one KV head (and its group of query heads) at a time, to bound host memory
         hq, hkv = c["hq"], c["hkv"]
-        for h in range(hq):
-            g = h * hkv // hq
-            ref, _ = orc.naive_attention_rows(_f64(q_rows[:, :, h:h + 1]), tok,
+        grp = hq // hkv
+        for g in range(hkv):
+            hs = slice(g * grp, (g + 1) * grp)
+            ref, _ = orc.naive_attention_rows(_f64(q_rows[:, :, hs]), tok,
                                               _f64(k_glob[:, :kmax, g:g + 1]),
                                               _f64(v_glob[:, :kmax, g:g + 1]), c["causal"])
-            worst = max(worst, float(np.abs(got[:, :, h:h + 1] - ref).max()))
+            worst = max(worst, float(np.abs(got[:, :, hs] - ref).max()))
     assert np.isfinite(got).all()
     assert worst <= tol, worst
     return worst
@@ -103,19 +104,46 @@ def test_c3_striped_gqa_rank7_sampled():
 
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
 def test_c4_one_million_tokens_rank7_sampled(layout):
-    say(f"c4: causal {layout}, 1,048,576 tokens, GQA 32/8, rank 7; 32 sampled rows")
+    say(f"c4: causal {layout}, 1,048,576 tokens, GQA 32/8, rank 7; 256 sampled rows x 32 heads")
     w = workloads.prepare("c4", layout, 7, device=DEV, keep_global=True)
     out, _ = _ring(w)
-    rows = workloads.sample_rows(w["cfg"]["block"], 32, seed=41)
-    say("c4", layout, "max-abs", _check_rows(out, w, rows, w["k_global"], w["v_global"]))
+    rows = workloads.sample_rows(w["cfg"]["block"], 256, seed=41)
+    say("c4", layout, "max-abs", _check_rows(out, w, rows, w["k_global"], w["v_global"],
+                                             per_head=True))
 
 
 def test_c5_video_noncausal_rank0_sampled():
-    say("c5: non-causal, 921,600 tokens (3600 frames x 256), 32 heads, rank 0; 24 sampled rows")
+    say("c5: non-causal, 921,600 tokens (3600 frames x 256), 32 heads, rank 0; "
+        "256 sampled rows x 32 heads")
     w = workloads.prepare("c5", "contiguous", 0, device=DEV, keep_global=True)
     out, _ = _ring(w)
-    rows = workloads.sample_rows(w["cfg"]["block"], 24, seed=51)
+    rows = workloads.sample_rows(w["cfg"]["block"], 256, seed=51)
     say("c5 max-abs", _check_rows(out, w, rows, w["k_global"], w["v_global"], per_head=True))
+
+
+def test_c2_in_order_staging_equals_side_stream(monkeypatch):
+    """Blocks of the 8192-token workload (8 MiB of K) are under the size from
+    which the library stages on the side stream: by default their copies run
+    in order on the compute stream. Forcing the side stream must give the
+    same bits, forward and backward."""
+    say("c2: default (in-order) staging vs forced side stream, rank 7, forward and backward")
+    w = workloads.prepare("c2", "contiguous", 7, device=DEV)
+    c = w["cfg"]
+    kw = dict(n_ring=8, causal=True, layout="contiguous", rank=7)
+    monkeypatch.delenv("RA_SIDE_STREAM_MIN_BYTES", raising=False)
+    out_a, lse_a = B.ra_ring_fwd(w["q"], w["k"], w["v"], **kw)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    dout = torch.randn(w["q"].shape, generator=g, device=DEV).to(w["q"].dtype)
+    grads_a = B.ra_ring_bwd(w["q"], w["k"], w["v"], out_a, dout, lse_a, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("RA_SIDE_STREAM_MIN_BYTES", "0")
+    out_b, lse_b = B.ra_ring_fwd(w["q"], w["k"], w["v"], **kw)
+    grads_b = B.ra_ring_bwd(w["q"], w["k"], w["v"], out_b, dout, lse_b, **kw)
+    torch.cuda.synchronize()
+    assert c["block"] * c["hkv"] * c["d"] * 2 * 2 < 32 << 20
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    for a, b in zip(grads_a, grads_b):
+        assert torch.equal(a, b)
 
 
 def test_c4_all_ranks_lse_consistency():

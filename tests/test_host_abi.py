@@ -80,6 +80,74 @@ def test_problem_validation_before_any_hip_call(L, kw, status):
     assert L.ra_ring_workspace_bytes(ctypes.byref(prob)) == 0
 
 
+def _grid_prob(**kw):
+    base = dict(dtype=B.RA_BF16, batch=1, hq=1, hkv=1, head_dim=128, q_len=1 << 20,
+                kv_len=1 << 20, n_ring=1, rank=0, causal=0, layout="contiguous")
+    base.update(kw)
+    return B.make_problem(**base)
+
+
+def _fwd_status(L, prob):
+    """Status of a forward call whose q pointer is NULL: a problem that passes
+    every launch check is rejected for the pointer ("q is NULL"), one that does
+    not for its grid; nothing is enqueued either way."""
+    st = L.ra_block_attn_partial(ctypes.byref(prob), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    return st, L.ra_last_error().decode()
+
+
+def _bwd_status(L, prob):
+    st = L.ra_block_attn_bwd(ctypes.byref(prob), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, None)
+    return st, L.ra_last_error().decode()
+
+
+@pytest.mark.parametrize("dtype,head_dim,batch,ok", [
+    # fp32 at d = 128: 64 rows and 256 work items per workgroup; 2^20 rows per
+    # head -> 16384 workgroups: 1024 heads fill 2^32 work items exactly (one too
+    # many), 1023 fit
+    (B.RA_F32, 128, 1024, False),
+    (B.RA_F32, 128, 1023, True),
+    (B.RA_F32, 128, 2048, False),   # was accepted when tiles were assumed to hold 128 rows
+    # fp32 at d = 16: 256 rows per workgroup of 256 work items
+    (B.RA_F32, 16, 4096, False),
+    (B.RA_F32, 16, 4095, True),
+    # bf16: 256 rows and 512 work items per workgroup
+    (B.RA_BF16, 128, 2048, False),
+    (B.RA_BF16, 128, 2047, True),
+])
+def test_forward_grid_checked_against_the_kernels_real_tiles(L, dtype, head_dim, batch, ok):
+    st, msg = _fwd_status(L, _grid_prob(dtype=dtype, head_dim=head_dim, batch=batch))
+    assert st == B.RA_ERR_INVALID_ARG
+    if ok:
+        assert "q is NULL" in msg, msg
+    else:
+        assert "too large for one launch of the attention kernel" in msg, msg
+    prob = _grid_prob(dtype=dtype, head_dim=head_dim, batch=batch)
+    st = L.ra_ring_fwd(ctypes.byref(prob), None, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, None)
+    assert st == B.RA_ERR_INVALID_ARG
+    assert ("q is NULL" in L.ra_last_error().decode()) == ok
+
+
+def test_backward_grid_checks_both_kernels(L):
+    # one query row against 2^26 keys per head: the dq launch is tiny, the dk/dv
+    # launch (128 keys and 256 work items per workgroup) needs 2^27 work items
+    # per head, so 32 heads are one too many for a dispatch
+    big = _grid_prob(head_dim=16, q_len=1, kv_len=1 << 26, batch=32)
+    st, msg = _bwd_status(L, big)
+    assert st == B.RA_ERR_INVALID_ARG and "dk/dv kernel" in msg, msg
+    st, msg = _fwd_status(L, big)   # the forward launch is small
+    assert st == B.RA_ERR_INVALID_ARG and "q is NULL" in msg, msg
+    st, msg = _bwd_status(L, _grid_prob(head_dim=16, q_len=1, kv_len=1 << 26, batch=31))
+    assert st == B.RA_ERR_INVALID_ARG and "q is NULL" in msg, msg
+    # the dq launch (256 rows, 512 work items) binds on a long query share
+    st, msg = _bwd_status(L, _grid_prob(batch=2048))
+    assert st == B.RA_ERR_INVALID_ARG and "dq kernel" in msg, msg
+    prob = _grid_prob(batch=2048)
+    st = L.ra_ring_bwd(ctypes.byref(prob), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                       FAKE, 1 << 40, None, None)
+    assert st == B.RA_ERR_INVALID_ARG and b"dq kernel" in L.ra_last_error()
+
+
 def test_bad_layout_and_causal_flags(L):
     prob = _prob()
     prob.layout = 5
@@ -172,17 +240,25 @@ def test_tile_classes_host_match_bruteforce(L, layout):
                     np.testing.assert_array_equal(mapped, want)
 
 
-def test_tile_classes_host_real_size_counts(L):
-    """1M-token share, 8 blocks of 131072, 128x128 tiles: host mirror counts vs
-    the oracle's closed-form counts for every (layout, rank, block)."""
-    blen, t = 131072, 128
-    for layout in ("contiguous", "striped"):
-        for r, j in itertools.product([0, 3, 7], range(8)):
-            prob = _prob(n_ring=8, rank=r, q_len=blen, kv_len=blen, layout=layout)
-            got = B.ra_tile_classes_host(prob, j, t, t)
-            counts = (int((got == B.RA_TILE_FULL).sum()), int((got == B.RA_TILE_PARTIAL).sum()),
-                      int((got == B.RA_TILE_SKIP).sum()))
-            assert counts == orc.tile_class_counts(layout, True, 8, r, j, blen, blen, t, t)
+def _counts(got):
+    c = np.bincount(got.ravel().astype(np.int64), minlength=3)
+    return int(c[B.RA_TILE_FULL]), int(c[B.RA_TILE_PARTIAL]), int(c[B.RA_TILE_SKIP])
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("tq,tk", [(128, 128), (64, 32)])
+def test_tile_classes_host_real_size_counts(L, layout, tq, tk):
+    """1M-token share, 8 blocks of 131072: the host mirror's class counts
+    equal the oracle's O(#tiles) counts for every rank and block, with
+    128 x 128 tiles and with the attention kernel's own unit (a workgroup's
+    256 rows are 64 positions x 4 heads at GQA 32/8; keys go in units of
+    32)."""
+    blen = 131072
+    for r, j in itertools.product(range(8), range(8)):
+        prob = _prob(n_ring=8, rank=r, q_len=blen, kv_len=blen, layout=layout)
+        got = B.ra_tile_classes_host(prob, j, tq, tk)
+        assert _counts(got) == orc.tile_class_counts(layout, True, 8, r, j, blen, blen, tq, tk), \
+            (layout, r, j)
 
 
 def test_tile_class_single(L):
@@ -206,16 +282,6 @@ def test_tile_classes_host_zigzag_match_bruteforce(L):
                     got = B.ra_tile_classes_host(prob, j, tq, tk)
                     want = orc.tile_classes_bruteforce("zigzag", causal, n, r, j, blen, blen, tq, tk)
                     np.testing.assert_array_equal(np.vectorize(_ORACLE_CLASS.get)(got), want)
-
-
-def test_tile_classes_host_zigzag_real_size_counts(L):
-    blen, t = 131072, 128
-    for r, j in itertools.product([0, 3, 7], range(8)):
-        prob = _prob(n_ring=8, rank=r, q_len=blen, kv_len=blen, layout="zigzag")
-        got = B.ra_tile_classes_host(prob, j, t, t)
-        counts = (int((got == B.RA_TILE_FULL).sum()), int((got == B.RA_TILE_PARTIAL).sum()),
-                  int((got == B.RA_TILE_SKIP).sum()))
-        assert counts == orc.tile_class_counts("zigzag", True, 8, r, j, blen, blen, t, t)
 
 
 PACKED = {

@@ -87,3 +87,38 @@ def test_sq_summary_busy_fraction_and_clock(tmp_path):
     assert s["mfma_executed_flops"] == 2000 * 32 * 32 * 16 * 2
     assert s["sq_insts_valu_per_mfma"] == pytest.approx(6.0)
     assert s["sq_insts_lds_per_mfma"] == pytest.approx(1.5)
+
+
+def test_trace_summary_checks_launches_fit_the_step(tmp_path):
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    rows = [dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=0, End_Timestamp=2_000_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=3_000_000, End_Timestamp=7_000_000)]
+    _write(str(tmp_path / "t.csv"), rows)
+    _write(str(tmp_path / "s.csv"), [dict(Name=attn, Calls=2, AverageNs=3e6, TotalDurationNs=6e6,
+                                          Percentage=100.0)])
+    s = P.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "s.csv"), 6.5, 2)
+    assert s["attention_avg_ms"] == pytest.approx(3.0)
+    assert s["attention_ms_per_step"] == pytest.approx(6.0)
+    with pytest.raises(ValueError):
+        P.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "s.csv"), 5.9, 2)
+
+
+def test_overlap_summary_splits_staged_and_nocopy_runs(tmp_path):
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    rows = []
+    t = 0
+    for run, dur in enumerate([10, 11, 10, 10, 12, 10]):  # staged, nocopy, staged, ...
+        for _ in range(2):
+            rows.append(dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=t * 1000,
+                             End_Timestamp=(t + dur) * 1000))
+            if run % 2 == 0:
+                rows.append(dict(Kernel_Name="__amd_rocclr_copyBuffer", Queue_Id=2,
+                                 Start_Timestamp=(t + 1) * 1000, End_Timestamp=(t + 3) * 1000))
+            t += dur + 1
+    _write(str(tmp_path / "t.csv"), rows)
+    o = P.overlap_summary(str(tmp_path / "t.csv"), 2)
+    assert o["runs"] == {"staged": 3, "nocopy": 3}
+    assert o["mean_attention_ms"]["staged"] == pytest.approx(2 * (10 + 10 + 12) / 3 / 1000)
+    assert o["mean_attention_ms"]["nocopy"] == pytest.approx(2 * (11 + 10 + 10) / 3 / 1000)
+    assert o["staged_minus_nocopy_ms"] == pytest.approx(2 * (32 - 31) / 3 / 1000)
+    assert o["staging_copies"] == 6
