@@ -146,7 +146,6 @@ void attn_bf16_mfma(AttnParams p) {
   using Dma = std::conditional_t<PAD, KvTileDma128<NW>, KvTileDma<D, NW>>;
   constexpr int TBX = PAD ? KvTile128::TB : T::TB;                // bytes per K (or V) tile
   constexpr int HALFX = PAD ? KvTile128::HALF : 32 * T::ROWB;     // bytes per 32 keys
-  constexpr int LOADS_PER_TILE = 2 * Dma::LPW;  // per wave: K and V
 
   extern __shared__ __align__(16) char smem[];
 
@@ -249,13 +248,13 @@ void attn_bf16_mfma(AttnParams p) {
     vbase = (grp >> 1) * KvTile128::SEGP + 16 * (4 * (sl >> 2) + lowc) + 8 * (sl & 1);
   }
 
+  // Two rings of kSlots 64-key tiles: K tile t in K slot t % kSlots, V tile t
+  // in V slot t % kSlots.
   auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * TBX; };
   auto slot_v = [&](int t) { return smem + (kSlots + (t & (kSlots - 1))) * TBX; };
   const Dma kv_dma(kv_len, kv_row_stride, wave, lane);
-  auto issue = [&](int t) {
-    kv_dma.issue(kg, t, slot_k(t));
-    kv_dma.issue(vg, t, slot_v(t));
-  };
+  auto issue_k = [&](int t) { kv_dma.issue(kg, t, slot_k(t)); };
+  auto issue_v = [&](int t) { kv_dma.issue(vg, t, slot_v(t)); };
   // Work is done in units of 32 keys: unit u is half u%2 of tile u/2. S(u)
   // is one 32x32 MFMA tile (16 registers per lane), P(u) two bf16x8 operands.
   // ks / vs: the LDS slot holding tile u/2 (the caller knows it).
@@ -347,49 +346,74 @@ void attn_bf16_mfma(AttnParams p) {
   };
 
   if (n_kt > 0) {
-    // Pipeline. Tiles live in a ring of kSlots LDS slots. Tile step t runs
-    // units 2t+1 and 2t+2, which read K only from tile t+1 and V only from
-    // tile t; it first issues the DMA of tile t+3 into the slot of tile t-1
-    // (whose last reader, the V of unit 2t, finished before the barrier that
-    // ended step t-1), and before its closing barrier each wave waits until
-    // at most one tile of its own loads (tile t+3) is in flight, i.e. tile
-    // t+2 has landed. Tiles past the last one are loaded (clamped rows) but
-    // never read, which keeps every wave's load count uniform.
+    // Pipeline. Unit u reads K of tile (u+1)/2 (for S(u+1)) and V of tile
+    // (u-1)/2 (for the P.V of P(u-1)). A step T runs units 4T+1 .. 4T+4, so
+    // it reads K tiles 2T+1, 2T+2 and V tiles 2T, 2T+1. It first issues the
+    // DMA of what step T+1 reads (K tiles 2T+3, 2T+4, V tiles 2T+2, 2T+3)
+    // into the slots whose last reader was step T-1, and ends with each wave
+    // waiting for its own loads and one barrier: the barrier makes the next
+    // step's tiles visible to every wave and frees this step's slots. One
+    // barrier per 128 keys, with the loads 128 keys ahead of their use.
+    // Tiles past the last one are loaded (clamped rows) but never read.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q fragments
-    issue(0);
-    issue(1);
-    issue(2);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
+    issue_k(0);
+    issue_k(1);
+    issue_v(0);
+    issue_v(1);
+    issue_k(2);
+    // K tile 0 (issued first) has landed once at most four tiles of this
+    // wave's loads are in flight
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * Dma::LPW) : "memory");
 
     const int n_u = (key_end + 31) / 32;  // units with any visible key
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
     qk(sA, 0, 0);
     unit(sA, sB, pB, pA, 0, n_u > 1, false, 0, 0);  // S(1) -> sB, P(0) -> pA
-    int t = 0;
-    for (; 2 * t + 3 < n_u; ++t) {
-      issue(t + 3);
-      const int s0 = t & (kSlots - 1), s1 = (t + 1) & (kSlots - 1);
-      unit(sB, sA, pA, pB, 2 * t + 1, true, true, s1, s0);  // S(2t+2) -> sA, P(2t+1) -> pB
-      unit(sA, sB, pB, pA, 2 * t + 2, true, true, s1, s0);  // S(2t+3) -> sB, P(2t+2) -> pA
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
-    }
-    // tail: units 2t+1 .. n_u-1 (at most two); every tile they read has
-    // landed once this wave's loads are complete and all waves met
+    // the rest of the prologue's tiles have landed, and K slot 0 (read by
+    // unit 0) is free for step 0's loads
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    int u = 2 * t + 1;
-    const int s0 = t & (kSlots - 1), s1 = (t + 1) & (kSlots - 1);
-    if (u < n_u) {
-      unit(sB, sA, pA, pB, u, u + 1 < n_u, true, s1, s0);
-      ++u;
-      if (u < n_u) {
-        unit(sA, sB, pB, pA, u, false, true, s1, s0);
-        pv(pA, u, s1);
+    // odd units keep S in sB and P in pB, even units S in sA and P in pA
+    int T = 0;
+    for (; 4 * T + 5 < n_u; ++T) {
+      issue_k(2 * T + 3);
+      issue_k(2 * T + 4);
+      issue_v(2 * T + 2);
+      issue_v(2 * T + 3);
+      unit(sB, sA, pA, pB, 4 * T + 1, true, true, 2 * T + 1, 2 * T);
+      unit(sA, sB, pB, pA, 4 * T + 2, true, true, 2 * T + 1, 2 * T);
+      unit(sB, sA, pA, pB, 4 * T + 3, true, true, 2 * T + 2, 2 * T + 1);
+      unit(sA, sB, pB, pA, 4 * T + 4, true, true, 2 * T + 2, 2 * T + 1);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // tail: units 4T+1 .. n_u-1 (at most four). Their K tiles (up to 2T+2) and
+    // V tiles (up to 2T+1) are in place; the P.V of unit 4T+4 would read V
+    // tile 2T+2, whose slot step T-1 freed.
+    const int u0 = 4 * T + 1;
+    if (u0 + 3 < n_u) {
+      issue_v(2 * T + 2);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (u0 < n_u) {
+      unit(sB, sA, pA, pB, u0, u0 + 1 < n_u, true, 2 * T + 1, 2 * T);
+      if (u0 + 1 < n_u) {
+        unit(sA, sB, pB, pA, u0 + 1, u0 + 2 < n_u, true, 2 * T + 1, 2 * T);
+        if (u0 + 2 < n_u) {
+          unit(sB, sA, pA, pB, u0 + 2, u0 + 3 < n_u, true, 2 * T + 2, 2 * T + 1);
+          if (u0 + 3 < n_u) {
+            unit(sA, sB, pB, pA, u0 + 3, false, true, 2 * T + 2, 2 * T + 1);
+            pv(pA, u0 + 3, 2 * T + 2);
+          } else {
+            pv(pB, u0 + 2, 2 * T + 1);
+          }
+        } else {
+          pv(pA, u0 + 1, 2 * T + 1);
+        }
       } else {
-        pv(pB, u - 1, s0);
+        pv(pB, u0, 2 * T);
       }
     } else {
-      pv(pA, u - 1, s0);
+      pv(pA, u0 - 1, 2 * T);
     }
   }
 
