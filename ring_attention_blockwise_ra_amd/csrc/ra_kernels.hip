@@ -125,7 +125,13 @@ struct KvTileDma128 {
 };
 
 template <int D, int NW>
-constexpr bool kPadTile = D == 128 && NW == 8;
+constexpr bool kPadTile = D == 128 && (NW == 8 || NW == 4);
+
+// K and V ring slots per workgroup: 4 + 4 with 8 waves (one workgroup per
+// CU), 2 + 2 with 4 waves, so that two workgroups share a CU (each with its
+// own rings, 65 KiB of LDS at d = 128).
+template <int NW>
+constexpr int kFwdSlots = NW == 4 ? 2 : kSlots;
 
 // The kernel's dynamic LDS (K/V tile ring) is sized at launch, so the
 // compiler cannot see that it limits the kernel to one workgroup per CU; with
@@ -250,8 +256,9 @@ void attn_bf16_mfma(AttnParams p) {
 
   // Two rings of kSlots 64-key tiles: K tile t in K slot t % kSlots, V tile t
   // in V slot t % kSlots.
-  auto slot_k = [&](int t) { return smem + (t & (kSlots - 1)) * TBX; };
-  auto slot_v = [&](int t) { return smem + (kSlots + (t & (kSlots - 1))) * TBX; };
+  constexpr int SL = kFwdSlots<NW>;
+  auto slot_k = [&](int t) { return smem + (t & (SL - 1)) * TBX; };
+  auto slot_v = [&](int t) { return smem + (SL + (t & (SL - 1))) * TBX; };
   const Dma kv_dma(kv_len, kv_row_stride, wave, lane);
   auto issue_k = [&](int t) { kv_dma.issue(kg, t, slot_k(t)); };
   auto issue_v = [&](int t) { kv_dma.issue(vg, t, slot_v(t)); };
@@ -345,7 +352,7 @@ void attn_bf16_mfma(AttnParams p) {
     rescale_o(alpha);
   };
 
-  if (n_kt > 0) {
+  if (NW == 8 && n_kt > 0) {
     // Pipeline. Unit u reads K of tile (u+1)/2 (for S(u+1)) and V of tile
     // (u-1)/2 (for the P.V of P(u-1)). A step T runs units 4T+1 .. 4T+4, so
     // it reads K tiles 2T+1, 2T+2 and V tiles 2T, 2T+1. It first issues the
@@ -414,6 +421,51 @@ void attn_bf16_mfma(AttnParams p) {
       }
     } else {
       pv(pA, u0 - 1, 2 * T);
+    }
+  }
+
+  if (NW != 8 && n_kt > 0) {
+    // Pipeline of a 4-wave workgroup (two per CU, 2 + 2 ring slots). A step t
+    // runs units 2t+1, 2t+2: it reads K tile t+1 and V tile t, and first
+    // issues K tile t+2 and V tile t+1 into the slots step t-1 read; it ends
+    // with each wave waiting for its own loads and one barrier.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q fragments
+    issue_k(0);
+    issue_k(1);
+    issue_v(0);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * Dma::LPW) : "memory");
+    const int n_u = (key_end + 31) / 32;
+    f32x16 sA, sB;
+    bf16x8 pA[2], pB[2];
+    qk(sA, 0, 0);
+    unit(sA, sB, pB, pA, 0, n_u > 1, false, 0, 0);
+    // K tile 1 and V tile 0 have landed, and K slot 0 (read by unit 0) is free
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    int t = 0;
+    for (; 2 * t + 3 < n_u; ++t) {
+      issue_k(t + 2);
+      issue_v(t + 1);
+      unit(sB, sA, pA, pB, 2 * t + 1, true, true, t + 1, t);
+      unit(sA, sB, pB, pA, 2 * t + 2, true, true, t + 1, t);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // tail: units 2t+1, 2t+2 (at most two) read K tile t+1 and V tile t; the
+    // P.V of unit 2t+2 reads V tile t+1, whose slot step t-1 freed
+    const int u0 = 2 * t + 1;
+    if (u0 + 1 < n_u) {
+      issue_v(t + 1);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (u0 < n_u) {
+      unit(sB, sA, pA, pB, u0, u0 + 1 < n_u, true, t + 1, t);
+      if (u0 + 1 < n_u) {
+        unit(sA, sB, pB, pA, u0 + 1, false, true, t + 1, t);
+        pv(pA, u0 + 1, t + 1);
+      } else {
+        pv(pB, u0, t);
+      }
+    } else {
+      pv(pA, u0 - 1, t);
     }
   }
 
@@ -670,8 +722,8 @@ template <int D, int NW>
 static hipError_t launch_bf16(AttnParams p, hipStream_t stream) {
   constexpr int ROWS = 32 * NW;
   const int64_t tiles = set_tiles(p, ROWS);
-  // ring of kSlots K tiles and kSlots V tiles
-  const size_t smem = 2 * kSlots * (size_t)(kPadTile<D, NW> ? KvTile128::TB : BfTile<D>::TB);
+  // the K ring then the V ring
+  const size_t smem = 2 * kFwdSlots<NW> * (size_t)(kPadTile<D, NW> ? KvTile128::TB : BfTile<D>::TB);
   auto kern = attn_bf16_mfma<D, NW>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
   if (e != hipSuccess) return e;
