@@ -205,6 +205,34 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
                       float* out, float* lse, void* workspace, size_t workspace_bytes,
                       void* compute_stream, void* copy_stream);
 
+/* Bytes of the static workspace of ra_ring_fwd_noalloc (per GPU). */
+#define RA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * ra_ring_fwd without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, results and stream
+ * contract as ra_ring_fwd (bit-identical outputs: the same kernels run);
+ * the workspace is instead a library-owned device array of
+ * RA_NOALLOC_WORKSPACE_BYTES on each GPU, held from the moment a device
+ * loads the library until the process ends.
+ *
+ * No call allocates or frees device memory. The first call on a device
+ * resolves the array's address there and creates the ring's event pool;
+ * later calls create nothing. Problems whose ra_ring_workspace_bytes
+ * exceeds RA_NOALLOC_WORKSPACE_BYTES return RA_ERR_WORKSPACE with nothing
+ * enqueued (about 64 MiB holds a share of 1024 tokens x 32 heads at
+ * head_dim 128 in bf16).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; nothing in it needs clearing, since every step overwrites what it
+ * reads. Calls whose work overlaps on one GPU (different streams, or
+ * several host threads) race on the array: serialise them.
+ */
+ra_status ra_ring_fwd_noalloc(const ra_problem* prob, const void* q, const void* k,
+                              const void* v, float* out, float* lse,
+                              void* compute_stream, void* copy_stream);
+
 /*
  * Causal tile scheduler, host mirror. Class of the pair (query rows
  * [a_lo, a_hi], keys [b_lo, b_hi]) of block j (local indices, inclusive;

@@ -36,8 +36,9 @@ EXPORTED = (
     "ra_block_attn_partial", "ra_merge_partials", "ra_finalize", "ra_ring_workspace_bytes",
     "ra_ring_fwd", "ra_tile_class_host", "ra_tile_classes_host", "ra_tile_classes_device",
     "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
-    "ra_rope_apply", "ra_last_error",
+    "ra_rope_apply", "ra_last_error", "ra_ring_fwd_noalloc",
 )
+RA_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class RaProblem(ctypes.Structure):
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
             L.ra_ring_bwd.restype = I32
             L.ra_rope_apply.argtypes = [PP, I32, I32, I32, I32, P, I32, P, I32, I32, P]
             L.ra_rope_apply.restype = I32
+            L.ra_ring_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P]
+            L.ra_ring_fwd_noalloc.restype = I32
             L.ra_last_error.argtypes = []
             L.ra_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -315,6 +318,35 @@ def ra_ring_fwd(q, k, v, *, n_ring: int, causal: bool, layout="contiguous", rank
         _check(lib().ra_ring_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                  _ptr(lse), _ptr(workspace), workspace.numel(), on.handle(), xs))
         on.done()
+    return out, lse
+
+
+def ra_ring_fwd_noalloc(q, k, v, *, n_ring: int, causal: bool, out, lse=None,
+                        layout="contiguous", rank: int = None, scale=None, compute_stream=None,
+                        copy_stream="auto", cu_seqlens=None, rope_theta=0.0):
+    """ra_ring_fwd on the library's static per-GPU workspace (no device
+    allocation by the library, none by this binding): the caller passes out
+    [b, lq, hq, d] float32 and optionally lse [b, lq, hq] float32. Problems
+    whose workspace exceeds RA_NOALLOC_WORKSPACE_BYTES raise RaError
+    (RA_ERR_WORKSPACE). Calls that overlap on one GPU race on that workspace."""
+    if rank is None:
+        rank = n_ring - 1
+    _need(q, "q")
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens, rope_theta)
+    b, lq, hq, d = q.shape
+    dev = q.device
+    _need(k, "k", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
+    _need(v, "v", q.dtype, (n_ring, b, prob.kv_len, prob.hkv, d), dev)
+    _need(out, "out", torch.float32, (b, lq, hq, d), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (b, lq, hq), dev)
+    with torch.cuda.device(dev):
+        if copy_stream == "auto":
+            copy_stream = side_stream(dev)
+        on = _OnStream(compute_stream, dev)
+        xs = ctypes.c_void_p(None) if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+        _check(lib().ra_ring_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(out), _ptr(lse), on.handle(), xs))
     return out, lse
 
 

@@ -510,6 +510,45 @@ struct Stager {
   }
 };
 
+// Workspace of ra_ring_fwd_noalloc: one file-scope device array per GPU,
+// allocated with the code object when a device loads the library and held
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is resolved once per device with
+// hipGetSymbolAddress and only that address is handed to kernels and copies.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static_assert(RA_NOALLOC_WORKSPACE_BYTES == kScratchBytes, "scratch size");
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch;  // device address of `scratch`, per device
+
+// Set-up of the allocation-free entry point on the current device (its first
+// call there): the array's device address and the ring's event pool, so
+// that later calls create nothing.
+ra_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(RA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    DeviceEvents* de = nullptr;
+    ra_status st = get_events(&de);
+    if (st != RA_OK) return st;
+    {
+      std::lock_guard<std::mutex> lk2(de->mu);
+      if ((st = init_events(de)) != RA_OK) return st;
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -747,6 +786,32 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
     if (st != RA_OK) return st;
     if ((st = check_fwd_grid(prob, s)) != RA_OK) return st;
     return ring_fwd_impl(prob, s, q, k, v, out, lse, workspace, workspace_bytes, compute_stream,
+                         copy_stream);
+  } catch (...) {
+    return fail(RA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+ra_status ra_ring_fwd_noalloc(const ra_problem* prob, const void* q, const void* k,
+                              const void* v, float* out, float* lse, void* compute_stream,
+                              void* copy_stream) {
+  try {
+    Shape s;
+    ra_status st = validate_problem(prob, &s);
+    if (st != RA_OK) return st;
+    if ((st = check_fwd_grid(prob, s)) != RA_OK) return st;
+    if ((st = check_ring_fwd_tensors(prob, s, q, k, v, out, lse)) != RA_OK) return st;
+    const size_t need = ws_layout(prob, s).total;
+    if (need > kScratchBytes)
+      return fail(RA_ERR_WORKSPACE,
+                  "the allocation-free ring needs %zu bytes of workspace; its static workspace "
+                  "holds %zu (use ra_ring_fwd with a caller workspace)",
+                  need, kScratchBytes);
+    if (s.rows == 0)
+      return ring_fwd_impl(prob, s, q, k, v, out, lse, nullptr, 0, compute_stream, copy_stream);
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != RA_OK) return st;
+    return ring_fwd_impl(prob, s, q, k, v, out, lse, ws, kScratchBytes, compute_stream,
                          copy_stream);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");

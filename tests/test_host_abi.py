@@ -148,6 +148,24 @@ def test_backward_grid_checks_both_kernels(L):
     assert st == B.RA_ERR_INVALID_ARG and b"dq kernel" in L.ra_last_error()
 
 
+def test_noalloc_validation_before_any_hip_call(L):
+    """The allocation-free ring refuses, with no HIP call, an invalid problem,
+    missing tensors, and a share whose workspace exceeds its static array."""
+    big = _prob(n_ring=8, rank=7, q_len=2048, kv_len=2048, hq=32, hkv=32, head_dim=128)
+    assert L.ra_ring_workspace_bytes(ctypes.byref(big)) > B.RA_NOALLOC_WORKSPACE_BYTES
+    assert L.ra_ring_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None, None, None) \
+        == B.RA_ERR_WORKSPACE
+    assert b"static workspace" in L.ra_last_error()
+    assert L.ra_ring_fwd_noalloc(ctypes.byref(big), None, FAKE, FAKE, FAKE, None, None, None) \
+        == B.RA_ERR_INVALID_ARG
+    assert b"q is NULL" in L.ra_last_error()
+    bad = _prob(hq=6, hkv=4)
+    assert L.ra_ring_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, None, None) \
+        == B.RA_ERR_INVALID_ARG
+    assert L.ra_ring_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, None, None, None) \
+        == B.RA_ERR_INVALID_ARG
+
+
 def test_bad_layout_and_causal_flags(L):
     prob = _prob()
     prob.layout = 5
