@@ -104,25 +104,52 @@ def overlap_summary(trace_csv: str, launches: int) -> dict:
     sequence); a run is "staged" when staging copies ran on another queue
     within its span. Returns the summed attention duration of each run, the
     mean per kind, and the staged-minus-no-copy difference: what concurrent
-    copies cost the kernels themselves."""
+    copies cost the kernels themselves. Also the compute queue's idle time
+    inside each run (its span minus the union of the kernels on that queue):
+    what the cross-stream waits add to the ring's critical path."""
     rows = _rows(trace_csv)
     attn = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Queue_Id"])
                   for r in rows if ATTN in r["Kernel_Name"])
     attn_q = {q for _, _, q in attn}
     copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
               if COPY in r["Kernel_Name"] and r["Queue_Id"] not in attn_q]
+    # every kernel on the attention's queue(s): the ring's critical path
+    lane = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                  if r["Queue_Id"] in attn_q)
     runs = {"staged": [], "nocopy": []}
+    gaps = {"staged": [], "nocopy": []}
     for i in range(0, len(attn) - launches + 1, launches):
         grp = attn[i:i + launches]
         a, b = grp[0][0], grp[-1][1]
         staged = any(s < b and e > a for s, e in copies)
-        runs["staged" if staged else "nocopy"].append(sum(e - s for s, e, _ in grp) / 1e6)
+        kind = "staged" if staged else "nocopy"
+        runs[kind].append(sum(e - s for s, e, _ in grp) / 1e6)
+        # idle time of the compute queue between the run's first and last
+        # attention launch: span minus the union of its kernels' busy time
+        busy, cur = 0, None
+        for s, e in lane:
+            if e <= a or s >= b:
+                continue
+            s, e = max(s, a), min(e, b)
+            if cur is None or s > cur[1]:
+                if cur is not None:
+                    busy += cur[1] - cur[0]
+                cur = [s, e]
+            else:
+                cur[1] = max(cur[1], e)
+        if cur is not None:
+            busy += cur[1] - cur[0]
+        gaps[kind].append((b - a - busy) / 1e6)
     mean = {k: (sum(v) / len(v) if v else None) for k, v in runs.items()}
+    gmean = {k: (sum(v) / len(v) if v else None) for k, v in gaps.items()}
     diff = (mean["staged"] - mean["nocopy"]) if None not in mean.values() else None
+    gdiff = (gmean["staged"] - gmean["nocopy"]) if None not in gmean.values() else None
     return dict(launches_per_run=launches, runs={k: len(v) for k, v in runs.items()},
                 attention_ms_per_run=runs, mean_attention_ms=mean,
                 staged_minus_nocopy_ms=diff,
                 staged_minus_nocopy_frac=(diff / mean["nocopy"]) if diff is not None else None,
+                queue_idle_ms_per_run=gaps, mean_queue_idle_ms=gmean,
+                queue_idle_staged_minus_nocopy_ms=gdiff,
                 staging_copies=len(copies),
                 staging_copy_ms=sum(e - s for s, e in copies) / 1e6)
 

@@ -122,3 +122,24 @@ def test_overlap_summary_splits_staged_and_nocopy_runs(tmp_path):
     assert o["mean_attention_ms"]["nocopy"] == pytest.approx(2 * (11 + 10 + 10) / 3 / 1000)
     assert o["staged_minus_nocopy_ms"] == pytest.approx(2 * (32 - 31) / 3 / 1000)
     assert o["staging_copies"] == 6
+
+
+def test_overlap_summary_queue_idle(tmp_path):
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    merge = "ra::merge_partials_kernel(long)"
+    # staged run: attn 0-10, gap 2, merge 12-13, gap 1, attn 14-24; copy on queue 2
+    # no-copy run: attn 30-40, merge 40-41, attn 41-51 (no gaps)
+    rows = [dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=0, End_Timestamp=10_000),
+            dict(Kernel_Name=merge, Queue_Id=1, Start_Timestamp=12_000, End_Timestamp=13_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=14_000, End_Timestamp=24_000),
+            dict(Kernel_Name="__amd_rocclr_copyBuffer", Queue_Id=2, Start_Timestamp=1_000,
+                 End_Timestamp=3_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=30_000, End_Timestamp=40_000),
+            dict(Kernel_Name=merge, Queue_Id=1, Start_Timestamp=40_000, End_Timestamp=41_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=41_000, End_Timestamp=51_000)]
+    _write(str(tmp_path / "t.csv"), rows)
+    o = P.overlap_summary(str(tmp_path / "t.csv"), 2)
+    assert o["runs"] == {"staged": 1, "nocopy": 1}
+    assert o["mean_queue_idle_ms"]["staged"] == pytest.approx(3e-3)
+    assert o["mean_queue_idle_ms"]["nocopy"] == pytest.approx(0.0)
+    assert o["queue_idle_staged_minus_nocopy_ms"] == pytest.approx(3e-3)
