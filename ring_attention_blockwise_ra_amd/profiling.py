@@ -118,6 +118,7 @@ def overlap_summary(trace_csv: str, launches: int) -> dict:
                   if r["Queue_Id"] in attn_q)
     runs = {"staged": [], "nocopy": []}
     gaps = {"staged": [], "nocopy": []}
+    seq = []   # (kind, attention ms, idle ms, copy ms) in trace order
     for i in range(0, len(attn) - launches + 1, launches):
         grp = attn[i:i + launches]
         a, b = grp[0][0], grp[-1][1]
@@ -140,6 +141,12 @@ def overlap_summary(trace_csv: str, launches: int) -> dict:
         if cur is not None:
             busy += cur[1] - cur[0]
         gaps[kind].append((b - a - busy) / 1e6)
+        cms = sum(min(e, b) - max(s, a) for s, e in copies if s < b and e > a) / 1e6
+        seq.append((kind, runs[kind][-1], gaps[kind][-1], cms))
+    # paired: each no-copy run against the staged run just before it (bench
+    # times them as interleaved pairs, so the two see the same clock)
+    pairs = [(p[1] - q[1], p[2] - q[2], p[3]) for p, q in zip(seq, seq[1:])
+             if p[0] == "staged" and q[0] == "nocopy"]
     mean = {k: (sum(v) / len(v) if v else None) for k, v in runs.items()}
     gmean = {k: (sum(v) / len(v) if v else None) for k, v in gaps.items()}
     diff = (mean["staged"] - mean["nocopy"]) if None not in mean.values() else None
@@ -150,8 +157,25 @@ def overlap_summary(trace_csv: str, launches: int) -> dict:
                 staged_minus_nocopy_frac=(diff / mean["nocopy"]) if diff is not None else None,
                 queue_idle_ms_per_run=gaps, mean_queue_idle_ms=gmean,
                 queue_idle_staged_minus_nocopy_ms=gdiff,
+                paired=_paired(pairs),
                 staging_copies=len(copies),
                 staging_copy_ms=sum(e - s for s, e in copies) / 1e6)
+
+
+def _paired(pairs):
+    """Median and range of the paired differences (attention time, queue idle
+    time) of staged minus no-copy runs, and the copy time of a staged run."""
+    if not pairs:
+        return None
+    med = lambda xs: sorted(xs)[len(xs) // 2] if len(xs) % 2 else \
+        (sorted(xs)[len(xs) // 2 - 1] + sorted(xs)[len(xs) // 2]) / 2  # noqa: E731
+    da, di, dc = zip(*pairs)
+    cost = med(da) + med(di)
+    return dict(pairs=len(pairs), attention_diff_ms=list(da), queue_idle_diff_ms=list(di),
+                attention_diff_ms_median=med(da), attention_diff_ms_range=[min(da), max(da)],
+                queue_idle_diff_ms_median=med(di), copy_ms_per_staged_run=med(dc),
+                cost_ms=cost,
+                efficiency=1.0 - max(0.0, cost) / med(dc) if med(dc) > 0 else None)
 
 
 def _counter_values(run_dir: str, counter: str):

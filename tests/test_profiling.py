@@ -122,6 +122,14 @@ def test_overlap_summary_splits_staged_and_nocopy_runs(tmp_path):
     assert o["mean_attention_ms"]["nocopy"] == pytest.approx(2 * (11 + 10 + 10) / 3 / 1000)
     assert o["staged_minus_nocopy_ms"] == pytest.approx(2 * (32 - 31) / 3 / 1000)
     assert o["staging_copies"] == 6
+    # interleaved pairs (staged run, then its no-copy run): 2 x (10-11, 10-10, 12-10) us
+    pr = o["paired"]
+    assert pr["pairs"] == 3
+    assert pr["attention_diff_ms"] == pytest.approx([-2e-3, 0.0, 4e-3])
+    assert pr["attention_diff_ms_median"] == pytest.approx(0.0)
+    assert pr["attention_diff_ms_range"] == pytest.approx([-2e-3, 4e-3])
+    assert pr["copy_ms_per_staged_run"] == pytest.approx(4e-3)   # two 2-us copies per run
+    assert pr["efficiency"] == pytest.approx(1.0)
 
 
 def test_overlap_summary_queue_idle(tmp_path):
@@ -143,3 +151,7 @@ def test_overlap_summary_queue_idle(tmp_path):
     assert o["mean_queue_idle_ms"]["staged"] == pytest.approx(3e-3)
     assert o["mean_queue_idle_ms"]["nocopy"] == pytest.approx(0.0)
     assert o["queue_idle_staged_minus_nocopy_ms"] == pytest.approx(3e-3)
+    pr = o["paired"]
+    assert pr["pairs"] == 1 and pr["queue_idle_diff_ms_median"] == pytest.approx(3e-3)
+    # attention time equal (20 us each); the 3 us of idle cost against 2 us of copies
+    assert pr["cost_ms"] == pytest.approx(3e-3) and pr["efficiency"] == pytest.approx(-0.5)
