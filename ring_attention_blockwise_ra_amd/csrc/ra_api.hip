@@ -163,10 +163,25 @@ ra_status check_grid(const ra_problem* p, const Shape& s, ra::TileShape t, const
   return RA_OK;
 }
 
-int env_waves();
+// Compute units of the GPU the launch shapes are chosen for (MI355X).
+constexpr int64_t kGpuCus = 256;
+
+// Waves per workgroup of the bf16 kernel: 8 (256 rows, one workgroup per CU,
+// two waves per SIMD) unless the 8-wave grid of this share has fewer
+// workgroups than the GPU has CUs; then 4 (128 rows, two workgroups per CU),
+// which spreads a small share over twice as many CUs (+10 % on 1024-token
+// blocks of 32 heads). RA_WAVES=4 or RA_WAVES=8 forces one (read at every
+// call, so that validation and launch of one call agree).
+int fwd_waves(const ra_problem* p, const Shape& s) {
+  const char* e = getenv("RA_WAVES");
+  if (e && (e[0] == '4' || e[0] == '8') && e[1] == 0) return e[0] - '0';
+  if (p->dtype != RA_BF16) return 8;
+  const int64_t wg8 = (int64_t)p->batch * p->hkv * tiles_per_head(p, s, ra::fwd_tile_shape(1, p->head_dim, 8));
+  return wg8 < kGpuCus ? 4 : 8;
+}
 
 ra_status check_fwd_grid(const ra_problem* p, const Shape& s) {
-  return check_grid(p, s, ra::fwd_tile_shape(p->dtype == RA_BF16, p->head_dim, env_waves()),
+  return check_grid(p, s, ra::fwd_tile_shape(p->dtype == RA_BF16, p->head_dim, fwd_waves(p, s)),
                     "attention");
 }
 
@@ -201,16 +216,6 @@ size_t side_stream_min_bytes() {
   const char* e = getenv("RA_SIDE_STREAM_MIN_BYTES");
   if (e && *e) return (size_t)strtoull(e, nullptr, 10);
   return size_t(32) << 20;
-}
-
-// Waves per workgroup of the bf16 kernel: 8 (two per SIMD) unless RA_WAVES=4.
-int env_waves() {
-  static int w = [] {
-    const char* e = getenv("RA_WAVES");
-    if (e && e[0] == '4' && e[1] == 0) return 4;
-    return 8;
-  }();
-  return w;
 }
 
 ra::AttnParams make_params(const ra_problem* p, const Shape& s, int32_t j, const void* q,
@@ -253,7 +258,7 @@ ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const 
     return RA_OK;
   }
   ra::AttnParams a = make_params(p, s, j, q, k, v, m, l, acc);
-  e = ra::launch_attention(a, p->dtype == RA_BF16, env_waves(), st);
+  e = ra::launch_attention(a, p->dtype == RA_BF16, fwd_waves(p, s), st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RA_OK;
 }

@@ -26,3 +26,18 @@ def side_stream_always():
         os.environ.pop("RA_SIDE_STREAM_MIN_BYTES", None)
     else:
         os.environ["RA_SIDE_STREAM_MIN_BYTES"] = old
+
+
+@pytest.fixture(scope="module", params=["8", "4"])
+def both_forward_shapes(request):
+    """Run the module once with 8-wave and once with 4-wave workgroups of the
+    bf16 attention kernel. The library picks 4 waves only for shares whose
+    8-wave grid has fewer workgroups than the GPU has CUs, which is every
+    small test here; forcing each keeps both kernels under every case."""
+    old = os.environ.get("RA_WAVES")
+    os.environ["RA_WAVES"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("RA_WAVES", None)
+    else:
+        os.environ["RA_WAVES"] = old

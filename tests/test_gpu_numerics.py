@@ -18,7 +18,7 @@ from ring_attention_blockwise_ra_amd import binding as B
 from ring_attention_blockwise_ra_amd import synth
 from ring_attention_blockwise_ra_amd.layout import blocks_from_global, share_tokens
 
-pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always")]
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always", "both_forward_shapes")]
 DEV = "cuda"
 TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 # lse = m + ln l: with bfloat16 inputs l sums weights rounded to bfloat16 (at

@@ -20,7 +20,7 @@ from ring_attention_blockwise_ra_amd import synth, workloads
 from ring_attention_blockwise_ra_amd.layout import (blocks_from_global, packed_blocks_from_global,
                                                     packed_share_tokens, share_tokens)
 
-pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always")]
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("side_stream_always", "both_forward_shapes")]
 TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 # lse = m + ln l, where l sums the weights after their rounding to bfloat16
 # (relative error <= 2^-9 each, so <= 2^-9 on l and on ln l); float32 inputs
