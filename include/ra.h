@@ -38,6 +38,19 @@
  *     exception crosses this ABI.
  *   - Empty problems (batch or q_len zero) return RA_OK and enqueue
  *     nothing.
+ *
+ * Environment (read at every call)
+ *   RA_DEBUG_SYNC=1    after its launches (the rings: after every step) an
+ *                      entry point waits for its streams and returns
+ *                      RA_ERR_HIP naming the launch or step of the first
+ *                      device error. Not for calls under graph capture.
+ *   RA_DEBUG_POISON=1  the rings fill each staging buffer with NaN right
+ *                      before the copy that refills it, so a read that
+ *                      races the copy yields NaN rather than a stale block.
+ *   RA_SIDE_STREAM_MIN_BYTES  see ra_ring_fwd.
+ *   RA_WAVES=4 | 8     waves per workgroup of the bf16 attention kernel
+ *                      (default: 8, or 4 when a launch of 8-wave workgroups
+ *                      would have fewer workgroups than the GPU has CUs).
  */
 #ifndef RA_H
 #define RA_H

@@ -43,6 +43,34 @@ ra_status hip_fail(hipError_t e, const char* what) {
   return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Debug switches, read at every call:
+//   RA_DEBUG_SYNC=1   each entry point waits for its streams after its
+//                     launches (the ring after every step) and reports the
+//                     first error with the launch or step it came from;
+//   RA_DEBUG_POISON=1 the ring fills each staging buffer with NaN right
+//                     before the copy that refills it, so a kernel that reads
+//                     a buffer before its copy has landed computes NaN
+//                     instead of a stale block.
+// Both are for eager calls: a stream cannot be waited on under graph capture.
+bool debug_on(const char* name) {
+  const char* e = getenv(name);
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+ra_status debug_sync(hipStream_t a, hipStream_t b, const char* what, int step) {
+  if (!debug_on("RA_DEBUG_SYNC")) return RA_OK;
+  hipError_t e = hipStreamSynchronize(a);
+  if (e == hipSuccess && b != nullptr && b != a) e = hipStreamSynchronize(b);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e == hipSuccess) return RA_OK;
+  if (step >= 0)
+    return fail(RA_ERR_HIP, "%s, step %d: %s", what, step, hipGetErrorString(e));
+  return hip_fail(e, what);
+}
+
+// 0x7FC0 is a bf16 quiet NaN and 0x7FC07FC0 a float32 one
+constexpr uint32_t kPoison = 0x7FC07FC0u;
+
 struct Shape {
   int64_t rows;        // batch * q_len * hq
   int64_t q_elems;     // batch * q_len * hq * d
@@ -444,6 +472,7 @@ struct Stager {
   DeviceEvents* de;
   hipStream_t cs, xs;
   bool sep, rope;
+  bool poison = debug_on("RA_DEBUG_POISON");
 
   int block_of(int step) const { return ((p->rank - step) % p->n_ring + p->n_ring) % p->n_ring; }
   bool staged(int step) const { return rope || step >= 1; }
@@ -460,6 +489,11 @@ struct Stager {
     const int j = block_of(step), b = step % 2;
     hipStream_t on = sep ? xs : cs;
     hipError_t e;
+    if (poison) {
+      if ((e = ra::launch_fill_u32(stage_k[b], (int64_t)blk, kPoison, on)) != hipSuccess ||
+          (e = ra::launch_fill_u32(stage_v[b], (int64_t)blk, kPoison, on)) != hipSuccess)
+        return hip_fail(e, "poison fill");
+    }
     if (rope) {
       ra::RopeParams r = make_rope(p, *s, false, j, p->hkv, p->dtype == RA_BF16,
                                    kbase + (size_t)j * blk, p->dtype == RA_BF16, stage_k[b],
@@ -588,8 +622,9 @@ ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j, cons
     if (overlap(m, rb, l, rb) || overlap(m, rb, acc, ab) || overlap(l, rb, acc, ab))
       return fail(RA_ERR_INVALID_ARG, "m, l and acc must not overlap");
     if (s.rows == 0) return RA_OK;
-    return enqueue_partial(prob, s, kv_block_j, q, k, v, m, l, acc,
-                           static_cast<hipStream_t>(hip_stream));
+    st = enqueue_partial(prob, s, kv_block_j, q, k, v, m, l, acc,
+                         static_cast<hipStream_t>(hip_stream));
+    return st != RA_OK ? st : debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "partial", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -632,7 +667,7 @@ ra_status ra_merge_partials(int64_t rows, int32_t head_dim, const float* m1, con
     hipError_t e = ra::launch_merge(rows, head_dim, m1, l1, acc1, m2, l2, acc2, m_out, l_out,
                                     acc_out, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "merge launch");
-    return RA_OK;
+    return debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "merge", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -659,7 +694,7 @@ ra_status ra_finalize(int64_t rows, int32_t head_dim, const float* m, const floa
     hipError_t e =
         ra::launch_finalize(rows, head_dim, m, l, acc, lse, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "finalize launch");
-    return RA_OK;
+    return debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "finalize", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -773,10 +808,11 @@ static ra_status ring_fwd_impl(const ra_problem* prob, const Shape& s, const voi
         }
       }
       if ((st = sg.done(step)) != RA_OK) return st;
+      if ((st = debug_sync(cs, sep ? xs : nullptr, "ring", step)) != RA_OK) return st;
     }
     e = ra::launch_finalize(s.rows, prob->head_dim, rm, rl, out, lse, cs);
     if (e != hipSuccess) return hip_fail(e, "finalize launch");
-    return RA_OK;
+    return debug_sync(cs, nullptr, "finalize", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -845,7 +881,7 @@ ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const
     hipError_t e = ra::launch_bwd_delta(rows, head_dim, dtype == RA_BF16, out, dout, delta,
                                         static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "delta launch");
-    return RA_OK;
+    return debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "delta", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -884,8 +920,10 @@ ra_status ra_block_attn_bwd(const ra_problem* prob, int32_t kv_block_j, const vo
           return fail(RA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
     }
     if (s.rows == 0) return RA_OK;
-    return enqueue_bwd(prob, s, kv_block_j, q, k, v, dout, lse, delta, dq, dk, dv,
-                       static_cast<hipStream_t>(hip_stream));
+    st = enqueue_bwd(prob, s, kv_block_j, q, k, v, dout, lse, delta, dq, dk, dv,
+                     static_cast<hipStream_t>(hip_stream));
+    return st != RA_OK ? st
+                       : debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "block backward", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -997,13 +1035,14 @@ ra_status ra_ring_bwd(const ra_problem* prob, const void* q, const void* k, cons
         if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
       }
       if ((st = sg.done(step)) != RA_OK) return st;
+      if ((st = debug_sync(cs, sep ? xs : nullptr, "backward ring", step)) != RA_OK) return st;
     }
     if (sg.rope) {  // dq with respect to the unrotated queries
       ra::RopeParams r = make_rope(prob, s, true, prob->rank, prob->hq, false, dq, false, dq, true,
                                    false);
       if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
     }
-    return RA_OK;
+    return debug_sync(cs, nullptr, "backward ring end", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -1042,7 +1081,7 @@ ra_status ra_rope_apply(const ra_problem* prob, int32_t target, int32_t block_j,
                                  accumulate != 0);
     hipError_t e = ra::launch_rope(r, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "rope launch");
-    return RA_OK;
+    return debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "rope", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
@@ -1115,7 +1154,7 @@ ra_status ra_tile_classes_device(const ra_problem* prob, int32_t kv_block_j, int
                                            s.packed ? &s.seg : nullptr, out_device,
                                            static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "tile_classes launch");
-    return RA_OK;
+    return debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "tile_classes", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }

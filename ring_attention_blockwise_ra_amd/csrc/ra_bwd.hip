@@ -1015,6 +1015,22 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(int64_t n4, f32x4* x) {
     x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(int64_t n4, u32x4* x, uint32_t value) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    x[i] = u32x4{value, value, value, value};
+}
+
+hipError_t launch_fill_u32(void* x, int64_t bytes, uint32_t value, hipStream_t stream) {
+  const int64_t n4 = bytes / 16;  // callers pass multiples of 16 bytes
+  if (n4 == 0) return hipSuccess;
+  int64_t blocks = (n4 + kThreads - 1) / kThreads;
+  if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, n4,
+                     reinterpret_cast<u32x4*>(x), value);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(float* x, int64_t n, hipStream_t stream) {
   const int64_t n4 = n / 4;  // callers pass multiples of 4 (rows * head_dim)
   int64_t blocks = (n4 + kThreads - 1) / kThreads;

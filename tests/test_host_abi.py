@@ -414,3 +414,18 @@ def test_rope_validation(L):
     assert L.ra_rope_apply(ctypes.byref(p), 1, 0, 2, B.RA_F32, FAKE, B.RA_BF16, FAKE, 0, 0, None) \
         == B.RA_ERR_INVALID_ARG  # in place with different dtypes
     assert L.ra_ring_workspace_bytes(ctypes.byref(p)) > L.ra_ring_workspace_bytes(ctypes.byref(_prob()))
+
+
+def test_debug_switches_leave_validation_before_any_hip_call(L, monkeypatch):
+    """RA_DEBUG_SYNC / RA_DEBUG_POISON only act after a call's launches: an
+    invalid call still returns its status with no HIP call (no GPU here)."""
+    monkeypatch.setenv("RA_DEBUG_SYNC", "1")
+    monkeypatch.setenv("RA_DEBUG_POISON", "1")
+    prob = _prob()
+    prob.layout = 5
+    assert _partial(L, prob) == B.RA_ERR_INVALID_ARG
+    big = _prob(n_ring=8, rank=7, q_len=2048, kv_len=2048, hq=32, hkv=32, head_dim=128)
+    assert L.ra_ring_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None, None, None) \
+        == B.RA_ERR_WORKSPACE
+    assert L.ra_merge_partials(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None) == B.RA_ERR_INVALID_ARG
