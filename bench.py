@@ -4,8 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
 
 A step is one full pass of the hot path over the workload: ra_ring_fwd for
-the share (8 ring steps: partial attention per block, staging copies on a
-side stream, merges, finalize). For the 1M-token causal workload (c4, the
+the share (8 ring steps: the attention kernel per block, the first block's
+partial starting the running state and every later one merged into it in
+the kernel's epilogue, staging copies on a side stream, finalize). For the 1M-token causal workload (c4, the
 default) a step runs the rank-7 share in both token layouts, contiguous then
 striped. Inputs are resident in HBM before timing starts.
 
@@ -13,8 +14,8 @@ Printed (one JSON line): TFLOP/s over causal-counted FLOPs (4*d per visible
 (query, key) pair per query head), the roofline of the attention kernel
 (its FLOPs per launch over its average launch time, measured with HIP events
 on its own stream), the cost of the staging copies (staged ring against the
-same kernels reading every block in place, interleaved pairs), merge-kernel
-HBM bandwidth, the backward ring, the other workloads' ring TFLOP/s (the
+same kernels reading every block in place, interleaved pairs), the HBM
+bandwidth of the standalone merge entry point, the backward ring, the other workloads' ring TFLOP/s (the
 8192-token sequence, the 131072-token striped share at every rank, the
 921,600-token video share), and the fp64 CPU oracle timed on a bounded sample
 of the same workload (a reported baseline, not a target) together with the
@@ -148,10 +149,12 @@ def kernel_leg(w):
         pairs = block_pairs(w["layout"], c["causal"], n, r, j, blen, w.get("seqlens"))
         if pairs == 0:
             continue
-        ms += timed(lambda: B.ra_block_attn_partial(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
-                                                     causal=c["causal"], layout=w["layout"],
-                                                     m=m, l=l, acc=acc,
-                                                     cu_seqlens=w.get("cu_seqlens")))
+        # as the ring runs it: the first block's partial starts the running
+        # state, every later block is merged into it by the same kernel
+        fn = B.ra_block_attn_partial if launches == 0 else B.ra_block_attn_accumulate
+        ms += timed(lambda: fn(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r, causal=c["causal"],
+                               layout=w["layout"], m=m, l=l, acc=acc,
+                               cu_seqlens=w.get("cu_seqlens")))
         flops += 4.0 * d * hq * b * pairs
         launches += 1
     return flops, ms, launches
@@ -210,9 +213,8 @@ def overlap_leg(w, out, lse, ws, reps=11, graph=False, copy_stream="auto"):
     n, r = c["n_ring"], w["rank"]
     q = w["q"]
     b, lq, hq, d = q.shape
-    pm = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device)
-    pl, rm, rl = torch.empty_like(pm), torch.empty_like(pm), torch.empty_like(pm)
-    pacc = torch.empty(b, lq, hq, d, dtype=torch.float32, device=q.device)
+    rm = torch.empty(b, lq, hq, dtype=torch.float32, device=q.device)
+    rl = torch.empty_like(rm)
 
     def nocopy():
         B.ra_block_attn_partial(q, w["k"][r], w["v"][r], r, n_ring=n, rank=r, causal=c["causal"],
@@ -222,10 +224,9 @@ def overlap_leg(w, out, lse, ws, reps=11, graph=False, copy_stream="auto"):
             j = (r - s) % n
             if block_pairs(w["layout"], c["causal"], n, r, j, c["block"], w.get("seqlens")) == 0:
                 continue
-            B.ra_block_attn_partial(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
-                                    causal=c["causal"], layout=w["layout"], m=pm, l=pl, acc=pacc,
-                                    cu_seqlens=w.get("cu_seqlens"))
-            B.ra_merge_partials(rm, rl, out, pm, pl, pacc, out=(rm, rl, out))
+            B.ra_block_attn_accumulate(q, w["k"][j], w["v"][j], j, n_ring=n, rank=r,
+                                       causal=c["causal"], layout=w["layout"], m=rm, l=rl,
+                                       acc=out, cu_seqlens=w.get("cu_seqlens"))
         B.ra_finalize(rm, rl, out, lse=lse)
 
     stage_k = torch.empty_like(w["k"][0])

@@ -156,6 +156,23 @@ ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j,
                                 float* m, float* l, float* acc, void* hip_stream);
 
 /*
+ * One ring step's running update ([UL] "How ring attention works": the
+ * running sums grow with each arriving block; [TS] "Tai sao no hoat dong":
+ * the running max and normaliser update, the output rescaled the same way):
+ * block j's partial, as ra_block_attn_partial defines it, merged into the
+ * running state (m, l, acc) in place with the merge of ra_merge_partials
+ * (the running state as input 1). One kernel: the block's partial never
+ * leaves the GPU's registers. m, l, acc are read and written; arguments,
+ * shapes, validation and overlap rules as ra_block_attn_partial. A block
+ * with no visible pair leaves the state unchanged (nothing is enqueued).
+ * ra_ring_fwd takes the first block with ra_block_attn_partial's kernel and
+ * every later one with this.
+ */
+ra_status ra_block_attn_accumulate(const ra_problem* prob, int32_t kv_block_j,
+                                   const void* q, const void* k, const void* v,
+                                   float* m, float* l, float* acc, void* hip_stream);
+
+/*
  * Online-softmax merge of two partials ([TS] "Tai sao no hoat dong"):
  *   m = max(m1, m2); a_i = exp(m_i - m) (0 when m_i = -inf);
  *   l = a1 l1 + a2 l2; acc = a1 acc1 + a2 acc2.
@@ -178,8 +195,8 @@ ra_status ra_finalize(int64_t rows, int32_t head_dim, const float* m, const floa
                       float* acc, float* lse, void* hip_stream);
 
 /* Workspace bytes ra_ring_fwd needs for this problem (0 on invalid input):
- * two staging buffers for K and two for V, one partial (m, l, acc) and the
- * running m and l (with rope_theta > 0 also the rotated queries). */
+ * two staging buffers for K and two for V and the running m and l (with
+ * rope_theta > 0 also the rotated queries); the running acc is out. */
 size_t ra_ring_workspace_bytes(const ra_problem* prob);
 
 /*

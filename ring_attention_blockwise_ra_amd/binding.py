@@ -36,7 +36,7 @@ EXPORTED = (
     "ra_block_attn_partial", "ra_merge_partials", "ra_finalize", "ra_ring_workspace_bytes",
     "ra_ring_fwd", "ra_tile_class_host", "ra_tile_classes_host", "ra_tile_classes_device",
     "ra_attn_bwd_delta", "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
-    "ra_rope_apply", "ra_last_error", "ra_ring_fwd_noalloc",
+    "ra_rope_apply", "ra_last_error", "ra_ring_fwd_noalloc", "ra_block_attn_accumulate",
 )
 RA_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
             PP = ctypes.POINTER(RaProblem)
             L.ra_block_attn_partial.argtypes = [PP, I32, P, P, P, P, P, P, P]
             L.ra_block_attn_partial.restype = I32
+            L.ra_block_attn_accumulate.argtypes = [PP, I32, P, P, P, P, P, P, P]
+            L.ra_block_attn_accumulate.restype = I32
             L.ra_merge_partials.argtypes = [I64, I32, P, P, P, P, P, P, P, P, P, P]
             L.ra_merge_partials.restype = I32
             L.ra_finalize.argtypes = [I64, I32, P, P, P, P, P]
@@ -225,6 +227,28 @@ def ra_block_attn_partial(q, k, v, kv_block_j: int, *, n_ring: int, rank: int, c
         _need(acc, "acc", torch.float32, (b, lq, hq, d), q.device)
         _check(lib().ra_block_attn_partial(ctypes.byref(prob), int(kv_block_j), _ptr(q), _ptr(k),
                                            _ptr(v), _ptr(m), _ptr(l), _ptr(acc), on.handle()))
+        on.done()
+    return m, l, acc
+
+
+def ra_block_attn_accumulate(q, k, v, kv_block_j: int, *, n_ring: int, rank: int, causal: bool,
+                             m, l, acc, layout="contiguous", scale=None, stream=None,
+                             cu_seqlens=None):
+    """Block kv_block_j's partial merged into the running (m, l, acc) in place
+    (see include/ra.h); returns (m, l, acc)."""
+    _need(q, "q")
+    prob = _qkv_problem(q, k, n_ring, rank, causal, layout, scale, cu_seqlens)
+    b, lq, hq, d = q.shape
+    _need(k, "k", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
+    _need(v, "v", q.dtype, (b, prob.kv_len, prob.hkv, d), q.device)
+    _need(m, "m", torch.float32, (b, lq, hq), q.device)
+    _need(l, "l", torch.float32, (b, lq, hq), q.device)
+    _need(acc, "acc", torch.float32, (b, lq, hq, d), q.device)
+    with torch.cuda.device(q.device):
+        on = _OnStream(stream, q.device)
+        _check(lib().ra_block_attn_accumulate(ctypes.byref(prob), int(kv_block_j), _ptr(q),
+                                              _ptr(k), _ptr(v), _ptr(m), _ptr(l), _ptr(acc),
+                                              on.handle()))
         on.done()
     return m, l, acc
 

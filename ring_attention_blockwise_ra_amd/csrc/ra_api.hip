@@ -273,19 +273,23 @@ ra::AttnParams make_params(const ra_problem* p, const Shape& s, int32_t j, const
   return a;
 }
 
-// Enqueue one block's partial into (m, l, acc). Skipped-block semantics: a
-// block with no visible pair (or no keys) yields the empty partial.
+// Enqueue one block's partial into (m, l, acc), or, with accumulate, merge
+// it into the running state (m, l, acc) in place. Skipped-block semantics: a
+// block with no visible pair (or no keys) yields the empty partial, which
+// leaves a running state unchanged.
 ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const void* q,
                           const void* k, const void* v, float* m, float* l, float* acc,
-                          hipStream_t st) {
+                          hipStream_t st, bool accumulate = false) {
   ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
   hipError_t e;
   if (g.kind == ra::kNoneVisible || p->kv_len == 0) {
+    if (accumulate) return RA_OK;
     e = ra::launch_fill_empty(s.rows, p->head_dim, m, l, acc, st);
     if (e != hipSuccess) return hip_fail(e, "fill_empty launch");
     return RA_OK;
   }
   ra::AttnParams a = make_params(p, s, j, q, k, v, m, l, acc);
+  a.accumulate = accumulate ? 1 : 0;
   e = ra::launch_attention(a, p->dtype == RA_BF16, fwd_waves(p, s), st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RA_OK;
@@ -391,7 +395,7 @@ BwdWsLayout bwd_ws_layout(const ra_problem* p, const Shape& s) {
 }
 
 struct WsLayout {
-  size_t stage_k[2], stage_v[2], pm, pl, pacc, rm, rl, qrot, total;
+  size_t stage_k[2], stage_v[2], rm, rl, qrot, total;
 };
 
 bool rope_on(const ra_problem* p) { return p->rope_theta > 0.f; }
@@ -400,7 +404,6 @@ WsLayout ws_layout(const ra_problem* p, const Shape& s) {
   WsLayout w{};
   const size_t blk = align256((size_t)s.kv_elems * s.elem);
   const size_t rowb = align256((size_t)s.rows * 4);
-  const size_t accb = align256((size_t)s.q_elems * 4);
   size_t off = 0;
   const bool staged = p->n_ring > 1 || rope_on(p);
   for (int i = 0; i < 2; ++i) {
@@ -409,9 +412,6 @@ WsLayout ws_layout(const ra_problem* p, const Shape& s) {
     w.stage_v[i] = off;
     off += staged ? blk : 0;
   }
-  w.pm = off; off += rowb;
-  w.pl = off; off += rowb;
-  w.pacc = off; off += p->n_ring > 1 ? accb : 0;
   w.rm = off; off += rowb;
   w.rl = off; off += rowb;
   w.qrot = off; off += rope_on(p) ? align256((size_t)s.q_elems * s.elem) : 0;
@@ -594,9 +594,9 @@ extern "C" {
 
 const char* ra_last_error(void) { return g_err.c_str(); }
 
-ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j, const void* q,
-                                const void* k, const void* v, float* m, float* l, float* acc,
-                                void* hip_stream) {
+static ra_status block_partial_entry(const ra_problem* prob, int32_t kv_block_j, const void* q,
+                                     const void* k, const void* v, float* m, float* l,
+                                     float* acc, void* hip_stream, bool accumulate) {
   try {
     Shape s;
     ra_status st = validate_problem(prob, &s);
@@ -623,11 +623,25 @@ ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j, cons
       return fail(RA_ERR_INVALID_ARG, "m, l and acc must not overlap");
     if (s.rows == 0) return RA_OK;
     st = enqueue_partial(prob, s, kv_block_j, q, k, v, m, l, acc,
-                         static_cast<hipStream_t>(hip_stream));
-    return st != RA_OK ? st : debug_sync(static_cast<hipStream_t>(hip_stream), nullptr, "partial", -1);
+                         static_cast<hipStream_t>(hip_stream), accumulate);
+    return st != RA_OK ? st
+                       : debug_sync(static_cast<hipStream_t>(hip_stream), nullptr,
+                                    accumulate ? "accumulate" : "partial", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+ra_status ra_block_attn_partial(const ra_problem* prob, int32_t kv_block_j, const void* q,
+                                const void* k, const void* v, float* m, float* l, float* acc,
+                                void* hip_stream) {
+  return block_partial_entry(prob, kv_block_j, q, k, v, m, l, acc, hip_stream, false);
+}
+
+ra_status ra_block_attn_accumulate(const ra_problem* prob, int32_t kv_block_j, const void* q,
+                                   const void* k, const void* v, float* m, float* l, float* acc,
+                                   void* hip_stream) {
+  return block_partial_entry(prob, kv_block_j, q, k, v, m, l, acc, hip_stream, true);
 }
 
 static ra_status check_alias_exact(const void* out, const void* in1, const void* in2, size_t n,
@@ -774,9 +788,6 @@ static ra_status ring_fwd_impl(const ra_problem* prob, const Shape& s, const voi
     if ((st = init_events(de)) != RA_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
-    float* pm = reinterpret_cast<float*>(ws + w.pm);
-    float* pl = reinterpret_cast<float*>(ws + w.pl);
-    float* pacc = reinterpret_cast<float*>(ws + w.pacc);
     float* rm = reinterpret_cast<float*>(ws + w.rm);
     float* rl = reinterpret_cast<float*>(ws + w.rl);
     Stager sg{prob, &s, static_cast<const char*>(k), static_cast<const char*>(v), blk,
@@ -796,17 +807,10 @@ static ra_status ring_fwd_impl(const ra_problem* prob, const Shape& s, const voi
       const void *kb = nullptr, *vb = nullptr;
       if ((st = sg.advance(step, &kb, &vb)) != RA_OK) return st;
       const int j = sg.block_of(step);
-      if (step == 0) {
-        // the local block's partial is the running state (m, l, out)
-        if ((st = enqueue_partial(prob, s, j, qx, kb, vb, rm, rl, out, cs)) != RA_OK) return st;
-      } else {
-        ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank, j);
-        if (g.kind != ra::kNoneVisible && prob->kv_len > 0) {
-          if ((st = enqueue_partial(prob, s, j, qx, kb, vb, pm, pl, pacc, cs)) != RA_OK) return st;
-          e = ra::launch_merge(s.rows, prob->head_dim, rm, rl, out, pm, pl, pacc, rm, rl, out, cs);
-          if (e != hipSuccess) return hip_fail(e, "merge launch");
-        }
-      }
+      // the local block's partial starts the running state (m, l, out); each
+      // later block's partial is merged into it by the attention kernel itself
+      if ((st = enqueue_partial(prob, s, j, qx, kb, vb, rm, rl, out, cs, step > 0)) != RA_OK)
+        return st;
       if ((st = sg.done(step)) != RA_OK) return st;
       if ((st = debug_sync(cs, sep ? xs : nullptr, "ring", step)) != RA_OK) return st;
     }

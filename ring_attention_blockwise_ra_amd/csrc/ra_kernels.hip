@@ -38,6 +38,19 @@
 
 namespace ra {
 
+// Online-softmax merge of two partials of one row ([TS] "Tai sao no hoat
+// dong"): with running maxima x1, x2 (natural units), the merged maximum mm
+// and the factors that bring each side's l and acc to it. An empty side
+// (-inf) weighs 0. Used by the merge kernel and by the attention kernels when
+// they merge their partial into the running state in place.
+struct MergeCoef {
+  float f1, f2, mm;
+};
+__device__ __forceinline__ MergeCoef merge_coef(float x1, float x2) {
+  const float mm = fmaxf(x1, x2);
+  return MergeCoef{(x1 == kNegInf) ? 0.f : expf(x1 - mm), (x2 == kNegInf) ? 0.f : expf(x2 - mm), mm};
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention partial
 // ---------------------------------------------------------------------------
@@ -479,25 +492,50 @@ void attn_bf16_mfma(AttnParams p) {
       for (int i = 0; i < 16; ++i) oacc[db][i] *= f;
   }
 
-  // ---- epilogue: (m, l, acc) with m in natural units --------------------
+  // ---- epilogue: (m, l, acc) with m in natural units, written, or merged
+  // into the running state (both lanes of a row read m and l before the
+  // half-0 lane writes them)
   const float lt = sum_xor32(l_run);
   if (row_ok) {
     const int64_t r = ((int64_t)b * p.q_len + tr.row0 + row_a) * p.hq + row_h;
-    if (half == 0) {
-      p.m[r] = (m_run == kNegInf) ? kNegInf : m_run * kLn2;
-      p.l[r] = lt;
-    }
+    const float mp = (m_run == kNegInf) ? kNegInf : m_run * kLn2;
     float* arow = p.acc + r * D;
+    if (p.accumulate) {
+      const float l_old = p.l[r];
+      const MergeCoef c = merge_coef(p.m[r], mp);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = db * 32 + 8 * u + 4 * half;
-        if (d < D) {
-          f32x4 o = {oacc[db][4 * u], oacc[db][4 * u + 1], oacc[db][4 * u + 2], oacc[db][4 * u + 3]};
-          *reinterpret_cast<f32x4*>(arow + d) = o;
+        for (int u = 0; u < 4; ++u) {
+          const int d = db * 32 + 8 * u + 4 * half;
+          if (d < D) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(arow + d);
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = c.f1 * w[i] + c.f2 * oacc[db][4 * u + i];
+            *reinterpret_cast<f32x4*>(arow + d) = o;
+          }
         }
+      if (half == 0) {
+        p.m[r] = c.mm;
+        p.l[r] = c.f1 * l_old + c.f2 * lt;
       }
+    } else {
+      if (half == 0) {
+        p.m[r] = mp;
+        p.l[r] = lt;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int d = db * 32 + 8 * u + 4 * half;
+          if (d < D) {
+            f32x4 o = {oacc[db][4 * u], oacc[db][4 * u + 1], oacc[db][4 * u + 2], oacc[db][4 * u + 3]};
+            *reinterpret_cast<f32x4*>(arow + d) = o;
+          }
+        }
+    }
   }
 }
 
@@ -581,15 +619,33 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
 
   if (ok) {
     const int64_t r = ((int64_t)b * p.q_len + tr.row0 + a) * p.hq + h;
-    if (part == 0) {
-      p.m[r] = (m == kNegInf) ? kNegInf : m * kLn2;
-      p.l[r] = l;
-    }
+    const float mp = (m == kNegInf) ? kNegInf : m * kLn2;
     float* arow = p.acc + r * D + part * DC;
+    if (p.accumulate) {  // the row's TPR threads share a wave: all read before part 0 writes
+      const float l_old = p.l[r];
+      const MergeCoef c = merge_coef(p.m[r], mp);
 #pragma unroll
-    for (int i = 0; i < DC; i += 4) {
-      f32x4 o = {acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
-      *reinterpret_cast<f32x4*>(arow + i) = o;
+      for (int i = 0; i < DC; i += 4) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(arow + i);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = c.f1 * w[e] + c.f2 * acc[i + e];
+        *reinterpret_cast<f32x4*>(arow + i) = o;
+      }
+      if (part == 0) {
+        p.m[r] = c.mm;
+        p.l[r] = c.f1 * l_old + c.f2 * l;
+      }
+    } else {
+      if (part == 0) {
+        p.m[r] = mp;
+        p.l[r] = l;
+      }
+#pragma unroll
+      for (int i = 0; i < DC; i += 4) {
+        f32x4 o = {acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+        *reinterpret_cast<f32x4*>(arow + i) = o;
+      }
     }
   }
 }
@@ -608,22 +664,17 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t row = i / vec_per_row;
-    const float x1 = m1[row], x2 = m2[row];
-    const float mm = fmaxf(x1, x2);
-    const float f1 = (x1 == kNegInf) ? 0.f : expf(x1 - mm);
-    const float f2 = (x2 == kNegInf) ? 0.f : expf(x2 - mm);
+    const MergeCoef c = merge_coef(m1[row], m2[row]);
     const f32x4 u = a1[i], w = a2[i];
     f32x4 o;
-    o[0] = f1 * u[0] + f2 * w[0];
-    o[1] = f1 * u[1] + f2 * w[1];
-    o[2] = f1 * u[2] + f2 * w[2];
-    o[3] = f1 * u[3] + f2 * w[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = c.f1 * u[e] + c.f2 * w[e];
     float nl = 0.f;
     const bool writer = (i - row * vec_per_row) == 0;
-    if (writer) nl = f1 * l1[row] + f2 * l2[row];
+    if (writer) nl = c.f1 * l1[row] + c.f2 * l2[row];
     ao[i] = o;
     if (writer) {
-      mo[row] = mm;
+      mo[row] = c.mm;
       lo[row] = nl;
     }
   }

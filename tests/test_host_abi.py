@@ -226,7 +226,7 @@ def test_ring_workspace_size_and_checks(L):
     rows = 2 * 1000 * 8
     def a(x):
         return (x + 255) // 256 * 256
-    want = 4 * a(blk) + 4 * a(rows * 4) + a(rows * 128 * 4)
+    want = 4 * a(blk) + 2 * a(rows * 4)
     assert got == want
     ws_small = ctypes.c_size_t(got - 1)
     buf = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(5)]
