@@ -499,11 +499,13 @@ struct Stager {
                                    kbase + (size_t)j * blk, p->dtype == RA_BF16, stage_k[b],
                                    false, false);
       e = ra::launch_rope(r, on);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice, on);
     } else {
-      e = hipMemcpyAsync(stage_k[b], kbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice, on);
+      // K and V of the block in one copy kernel (one launch per step)
+      e = ra::launch_copy2(stage_k[b], kbase + (size_t)j * blk, stage_v[b],
+                           vbase + (size_t)j * blk, (int64_t)blk, on);
     }
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(stage_v[b], vbase + (size_t)j * blk, blk, hipMemcpyDeviceToDevice, on);
     if (e != hipSuccess) return hip_fail(e, "staging copy");
     if (sep && (e = hipEventRecord(de->copy_done[b], xs)) != hipSuccess)
       return hip_fail(e, "hipEventRecord");

@@ -1031,6 +1031,33 @@ hipError_t launch_fill_u32(void* x, int64_t bytes, uint32_t value, hipStream_t s
   return hipGetLastError();
 }
 
+// dst_a <- src_a and dst_b <- src_b, n4 16-byte vectors each, in one launch
+// (the two staging copies of a ring step)
+__global__ __launch_bounds__(kThreads) void copy2_kernel(int64_t n4, const u32x4* __restrict__ sa,
+                                                        u32x4* __restrict__ da,
+                                                        const u32x4* __restrict__ sb,
+                                                        u32x4* __restrict__ db) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n4; i += stride) {
+    if (i < n4)
+      da[i] = sa[i];
+    else
+      db[i - n4] = sb[i - n4];
+  }
+}
+
+hipError_t launch_copy2(void* dst_a, const void* src_a, void* dst_b, const void* src_b,
+                        int64_t bytes, hipStream_t stream) {
+  const int64_t n4 = bytes / 16;  // callers pass multiples of 16 bytes
+  if (n4 == 0) return hipSuccess;
+  int64_t blocks = (2 * n4 + kThreads - 1) / kThreads;
+  if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+  hipLaunchKernelGGL(copy2_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, n4,
+                     reinterpret_cast<const u32x4*>(src_a), reinterpret_cast<u32x4*>(dst_a),
+                     reinterpret_cast<const u32x4*>(src_b), reinterpret_cast<u32x4*>(dst_b));
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(float* x, int64_t n, hipStream_t stream) {
   const int64_t n4 = n / 4;  // callers pass multiples of 4 (rows * head_dim)
   int64_t blocks = (n4 + kThreads - 1) / kThreads;

@@ -69,6 +69,10 @@ struct BwdParams {
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t stream);
 // x[0 .. n) = 0 (n a multiple of 4), a kernel rather than a memset.
 hipError_t launch_zero(float* x, int64_t n, hipStream_t stream);
+// dst_a[0 .. bytes) = src_a and dst_b[0 .. bytes) = src_b in one kernel launch
+// (bytes a multiple of 16; the regions must not overlap)
+hipError_t launch_copy2(void* dst_a, const void* src_a, void* dst_b, const void* src_b,
+                        int64_t bytes, hipStream_t stream);
 // every 32-bit word of x[0 .. bytes) = value (bytes a multiple of 16), a kernel
 hipError_t launch_fill_u32(void* x, int64_t bytes, uint32_t value, hipStream_t stream);
 // delta[r] = sum_d dout[r, d] * out[r, d]; dout in the input dtype.

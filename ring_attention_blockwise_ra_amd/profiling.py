@@ -35,7 +35,12 @@ import sys
 from collections import defaultdict
 
 ATTN = "attn_bf16_mfma"
-COPY = "copyBuffer"
+COPY = "copyBuffer"          # the runtime's device copy (calibration copies, rotary-path V)
+STAGE_COPY = "copy2_kernel"  # the ring's staging copy of K and V
+
+
+def _is_copy(name: str) -> bool:
+    return COPY in name or STAGE_COPY in name
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["ring_attention_blockwise_ra_amd/csrc/ra_kernels.hip",
                   "ring_attention_blockwise_ra_amd/csrc/ra_device.h",
@@ -66,7 +71,7 @@ def trace_summary(trace_csv: str, stats_csv: str, ms_per_step: float | None = No
     attn_q = {r["Queue_Id"] for r in attn}
     spans = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in attn)
     # staging copies: blit-copy kernels on a queue the attention kernel does not use
-    copies = [r for r in rows if COPY in r["Kernel_Name"] and r["Queue_Id"] not in attn_q]
+    copies = [r for r in rows if _is_copy(r["Kernel_Name"]) and r["Queue_Id"] not in attn_q]
     tot = hidden = 0
     for r in copies:
         s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
@@ -77,7 +82,7 @@ def trace_summary(trace_csv: str, stats_csv: str, ms_per_step: float | None = No
     for r in _rows(stats_csv):
         name = r["Name"]
         for key in ("attn_bf16_mfma", "attn_f32_fma", "merge_partials", "finalize_kernel",
-                    "fill_empty", COPY):
+                    "fill_empty", COPY, STAGE_COPY):
             if key in name:
                 stats[name[:80]] = dict(calls=int(r["Calls"]), avg_ms=float(r["AverageNs"]) / 1e6,
                                         total_ms=float(r["TotalDurationNs"]) / 1e6,
@@ -112,7 +117,7 @@ def overlap_summary(trace_csv: str, launches: int) -> dict:
                   for r in rows if ATTN in r["Kernel_Name"])
     attn_q = {q for _, _, q in attn}
     copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
-              if COPY in r["Kernel_Name"] and r["Queue_Id"] not in attn_q]
+              if _is_copy(r["Kernel_Name"]) and r["Queue_Id"] not in attn_q]
     # every kernel on the attention's queue(s): the ring's critical path
     lane = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
                   if r["Queue_Id"] in attn_q)

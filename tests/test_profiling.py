@@ -155,3 +155,19 @@ def test_overlap_summary_queue_idle(tmp_path):
     assert pr["pairs"] == 1 and pr["queue_idle_diff_ms_median"] == pytest.approx(3e-3)
     # attention time equal (20 us each); the 3 us of idle cost against 2 us of copies
     assert pr["cost_ms"] == pytest.approx(3e-3) and pr["efficiency"] == pytest.approx(-0.5)
+
+
+def test_staging_copy_kernel_counts_as_a_copy(tmp_path):
+    """The ring stages K and V with its own copy kernel; the summaries count it
+    as a staging copy like the runtime's copy."""
+    attn = "void ra::attn_bf16_mfma<128, 8>(ra::AttnParams)"
+    stage = "ra::copy2_kernel(long, unsigned int __vector(4) const*, ...)"
+    rows = [dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=0, End_Timestamp=10_000),
+            dict(Kernel_Name=stage, Queue_Id=2, Start_Timestamp=1_000, End_Timestamp=3_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=10_000, End_Timestamp=20_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=30_000, End_Timestamp=40_000),
+            dict(Kernel_Name=attn, Queue_Id=1, Start_Timestamp=40_000, End_Timestamp=50_000)]
+    _write(str(tmp_path / "t.csv"), rows)
+    o = P.overlap_summary(str(tmp_path / "t.csv"), 2)
+    assert o["runs"] == {"staged": 1, "nocopy": 1}
+    assert o["staging_copies"] == 1 and o["staging_copy_ms"] == pytest.approx(2e-3)
