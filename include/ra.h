@@ -251,8 +251,8 @@ ra_status ra_ring_fwd(const ra_problem* prob, const void* q, const void* k, cons
  * resolves the array's address there and creates the ring's event pool;
  * later calls create nothing. Problems whose ra_ring_workspace_bytes
  * exceeds RA_NOALLOC_WORKSPACE_BYTES return RA_ERR_WORKSPACE with nothing
- * enqueued (about 64 MiB holds a share of 1024 tokens x 32 heads at
- * head_dim 128 in bf16).
+ * enqueued (64 MiB holds a bf16 share of about 2000 tokens with 32 KV
+ * heads at head_dim 128, about 7900 with 8 KV heads).
  *
  * Every call on one GPU shares that GPU's array and leaves its contents
  * behind; nothing in it needs clearing, since every step overwrites what it
