@@ -277,9 +277,12 @@ ra::AttnParams make_params(const ra_problem* p, const Shape& s, int32_t j, const
 // it into the running state (m, l, acc) in place. Skipped-block semantics: a
 // block with no visible pair (or no keys) yields the empty partial, which
 // leaves a running state unchanged.
+// finalize: the launch also divides, acc <- acc / l and lse <- m + ln l (the
+// ring's last launch; lse may be null).
 ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const void* q,
                           const void* k, const void* v, float* m, float* l, float* acc,
-                          hipStream_t st, bool accumulate = false) {
+                          hipStream_t st, bool accumulate = false, bool finalize = false,
+                          float* lse = nullptr) {
   ra::BlockGeom g = ra::block_geom(p->causal, p->layout, p->rank, j);
   hipError_t e;
   if (g.kind == ra::kNoneVisible || p->kv_len == 0) {
@@ -290,6 +293,8 @@ ra_status enqueue_partial(const ra_problem* p, const Shape& s, int32_t j, const 
   }
   ra::AttnParams a = make_params(p, s, j, q, k, v, m, l, acc);
   a.accumulate = accumulate ? 1 : 0;
+  a.finalize = finalize ? 1 : 0;
+  a.lse = lse;
   e = ra::launch_attention(a, p->dtype == RA_BF16, fwd_waves(p, s), st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RA_OK;
@@ -804,6 +809,15 @@ static ra_status ring_fwd_impl(const ra_problem* prob, const Shape& s, const voi
       if ((e = ra::launch_rope(r, cs)) != hipSuccess) return hip_fail(e, "rope launch");
       qx = qr;
     }
+    // the last step that launches the attention kernel also divides (no
+    // separate finalize); a ring whose only launch is the empty fill of
+    // step 0 keeps the finalize kernel
+    int last = -1;
+    for (int step = 0; step < n; ++step) {
+      const ra::BlockGeom g = ra::block_geom(prob->causal, prob->layout, prob->rank,
+                                             sg.block_of(step));
+      if (g.kind != ra::kNoneVisible && prob->kv_len > 0) last = step;
+    }
     if ((st = sg.start()) != RA_OK) return st;
     for (int step = 0; step < n; ++step) {
       const void *kb = nullptr, *vb = nullptr;
@@ -811,13 +825,16 @@ static ra_status ring_fwd_impl(const ra_problem* prob, const Shape& s, const voi
       const int j = sg.block_of(step);
       // the local block's partial starts the running state (m, l, out); each
       // later block's partial is merged into it by the attention kernel itself
-      if ((st = enqueue_partial(prob, s, j, qx, kb, vb, rm, rl, out, cs, step > 0)) != RA_OK)
+      if ((st = enqueue_partial(prob, s, j, qx, kb, vb, rm, rl, out, cs, step > 0, step == last,
+                                lse)) != RA_OK)
         return st;
       if ((st = sg.done(step)) != RA_OK) return st;
       if ((st = debug_sync(cs, sep ? xs : nullptr, "ring", step)) != RA_OK) return st;
     }
-    e = ra::launch_finalize(s.rows, prob->head_dim, rm, rl, out, lse, cs);
-    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    if (last < 0) {
+      e = ra::launch_finalize(s.rows, prob->head_dim, rm, rl, out, lse, cs);
+      if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    }
     return debug_sync(cs, nullptr, "finalize", -1);
   } catch (...) {
     return fail(RA_ERR_HIP, "unexpected C++ exception");

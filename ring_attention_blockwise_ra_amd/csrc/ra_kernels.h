@@ -27,6 +27,8 @@ struct AttnParams {
   int32_t group;        // hq / hkv
   int32_t packed;       // 1: segment s also owns keys [off[s], off[s+1])
   int32_t accumulate;   // 1: merge the block's partial into (m, l, acc) in place
+  int32_t finalize;     // 1: also divide: acc <- acc / l, lse <- m + ln l (lse may be null)
+  float* lse;           // [batch, q_len, hq] when finalize
   int32_t tiles_total;  // set by the launcher: row tiles over all segments
   int32_t geom_kind;    // ra::BlockKind
   int32_t geom_delta;

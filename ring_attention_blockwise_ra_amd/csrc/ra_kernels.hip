@@ -51,6 +51,14 @@ __device__ __forceinline__ MergeCoef merge_coef(float x1, float x2) {
   return MergeCoef{(x1 == kNegInf) ? 0.f : expf(x1 - mm), (x2 == kNegInf) ? 0.f : expf(x2 - mm), mm};
 }
 
+// The final divide of one row ([UL] "How ring attention works"): the factor
+// that turns acc into the output, and lse = m + ln l (-inf for l = 0), as
+// finalize_kernel computes them.
+__device__ __forceinline__ float finalize_inv(float l) { return l > 0.f ? 1.0f / l : 0.f; }
+__device__ __forceinline__ float finalize_lse(float m, float l) {
+  return l > 0.f ? m + logf(l) : kNegInf;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention partial
 // ---------------------------------------------------------------------------
@@ -494,47 +502,48 @@ void attn_bf16_mfma(AttnParams p) {
 
   // ---- epilogue: (m, l, acc) with m in natural units, written, or merged
   // into the running state (both lanes of a row read m and l before the
-  // half-0 lane writes them)
+  // half-0 lane writes them); with finalize the divided output and lse
   const float lt = sum_xor32(l_run);
   if (row_ok) {
     const int64_t r = ((int64_t)b * p.q_len + tr.row0 + row_a) * p.hq + row_h;
     const float mp = (m_run == kNegInf) ? kNegInf : m_run * kLn2;
     float* arow = p.acc + r * D;
+    float f1 = 0.f, f2 = 1.0f, mo = mp, lo = lt;
     if (p.accumulate) {
       const float l_old = p.l[r];
       const MergeCoef c = merge_coef(p.m[r], mp);
+      f1 = c.f1;
+      f2 = c.f2;
+      mo = c.mm;
+      lo = c.f1 * l_old + c.f2 * lt;
+    }
+    const float inv = p.finalize ? finalize_inv(lo) : 1.0f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int d = db * 32 + 8 * u + 4 * half;
-          if (d < D) {
+      for (int u = 0; u < 4; ++u) {
+        const int d = db * 32 + 8 * u + 4 * half;
+        if (d < D) {
+          f32x4 o;
+          if (p.accumulate) {
             const f32x4 w = *reinterpret_cast<const f32x4*>(arow + d);
-            f32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = c.f1 * w[i] + c.f2 * oacc[db][4 * u + i];
-            *reinterpret_cast<f32x4*>(arow + d) = o;
+            for (int i = 0; i < 4; ++i) o[i] = f1 * w[i] + f2 * oacc[db][4 * u + i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = oacc[db][4 * u + i];
           }
-        }
-      if (half == 0) {
-        p.m[r] = c.mm;
-        p.l[r] = c.f1 * l_old + c.f2 * lt;
-      }
-    } else {
-      if (half == 0) {
-        p.m[r] = mp;
-        p.l[r] = lt;
-      }
+          if (p.finalize) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int d = db * 32 + 8 * u + 4 * half;
-          if (d < D) {
-            f32x4 o = {oacc[db][4 * u], oacc[db][4 * u + 1], oacc[db][4 * u + 2], oacc[db][4 * u + 3]};
-            *reinterpret_cast<f32x4*>(arow + d) = o;
+            for (int i = 0; i < 4; ++i) o[i] *= inv;
           }
+          *reinterpret_cast<f32x4*>(arow + d) = o;
         }
+      }
+    if (half == 0) {
+      p.m[r] = mo;
+      p.l[r] = lo;
+      if (p.finalize && p.lse != nullptr) p.lse[r] = finalize_lse(mo, lo);
     }
   }
 }
@@ -621,31 +630,38 @@ __global__ __launch_bounds__(kThreads) void attn_f32_fma(AttnParams p) {
     const int64_t r = ((int64_t)b * p.q_len + tr.row0 + a) * p.hq + h;
     const float mp = (m == kNegInf) ? kNegInf : m * kLn2;
     float* arow = p.acc + r * D + part * DC;
-    if (p.accumulate) {  // the row's TPR threads share a wave: all read before part 0 writes
+    // the row's TPR threads share a wave: all read m and l before part 0 writes
+    float f1 = 0.f, f2 = 1.0f, mo = mp, lo = l;
+    if (p.accumulate) {
       const float l_old = p.l[r];
       const MergeCoef c = merge_coef(p.m[r], mp);
+      f1 = c.f1;
+      f2 = c.f2;
+      mo = c.mm;
+      lo = c.f1 * l_old + c.f2 * l;
+    }
+    const float inv = p.finalize ? finalize_inv(lo) : 1.0f;
 #pragma unroll
-      for (int i = 0; i < DC; i += 4) {
+    for (int i = 0; i < DC; i += 4) {
+      f32x4 o;
+      if (p.accumulate) {
         const f32x4 w = *reinterpret_cast<const f32x4*>(arow + i);
-        f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = c.f1 * w[e] + c.f2 * acc[i + e];
-        *reinterpret_cast<f32x4*>(arow + i) = o;
-      }
-      if (part == 0) {
-        p.m[r] = c.mm;
-        p.l[r] = c.f1 * l_old + c.f2 * l;
-      }
-    } else {
-      if (part == 0) {
-        p.m[r] = mp;
-        p.l[r] = l;
-      }
+        for (int e = 0; e < 4; ++e) o[e] = f1 * w[e] + f2 * acc[i + e];
+      } else {
 #pragma unroll
-      for (int i = 0; i < DC; i += 4) {
-        f32x4 o = {acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
-        *reinterpret_cast<f32x4*>(arow + i) = o;
+        for (int e = 0; e < 4; ++e) o[e] = acc[i + e];
       }
+      if (p.finalize) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= inv;
+      }
+      *reinterpret_cast<f32x4*>(arow + i) = o;
+    }
+    if (part == 0) {
+      p.m[r] = mo;
+      p.l[r] = lo;
+      if (p.finalize && p.lse != nullptr) p.lse[r] = finalize_lse(mo, lo);
     }
   }
 }
@@ -688,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(int64_t rows, int ve
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t row = i / vec_per_row;
     const float L = l[row];
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    const float inv = finalize_inv(L);
     f32x4 x = acc[i];
     x[0] *= inv;
     x[1] *= inv;
@@ -696,7 +712,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(int64_t rows, int ve
     x[3] *= inv;
     acc[i] = x;
     if (lse != nullptr && (i - row * vec_per_row) == 0)
-      lse[row] = L > 0.f ? m[row] + logf(L) : kNegInf;
+      lse[row] = finalize_lse(m[row], L);
   }
 }
 
