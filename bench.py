@@ -551,6 +551,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+        # the standalone merge at this share, so that the same counter runs
+        # measure its bytes too (the ring itself launches none)
+        merge_leg(ws_list[0], reps=1)
+        torch.cuda.synchronize()
+        log("[bench] merge for the counters done")
 
     def step():
         for w in ws_list:
