@@ -80,6 +80,10 @@ int main(void) {
   odd.head_dim = 96;
   CHECK(ra_ring_workspace_bytes(&odd) == 0);
   CHECK(ra_block_attn_partial(&odd, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL) != RA_OK);
+  /* the running update validates exactly as the partial does */
+  CHECK(ra_block_attn_accumulate(&p, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == RA_ERR_INVALID_ARG);
+  CHECK(ra_block_attn_accumulate(&odd, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == RA_ERR_UNSUPPORTED);
+  CHECK(ra_block_attn_accumulate(&p, 4, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == RA_ERR_INVALID_ARG);
 
   if (failures == 0) printf("ok\n");
   return failures == 0 ? 0 : 1;
