@@ -216,6 +216,11 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob);
  * place; for s >= 1 block j is first copied into staging buffer s % 2 on
  * copy_stream while step s-1 computes on compute_stream (events order the
  * copy after the last read of that buffer, and the compute after the copy).
+ * Step 0's partial starts the running state (m, l in the workspace, acc in
+ * out); every later computed block is merged into it by the same kernel
+ * (ra_block_attn_accumulate), and the last computed block's kernel also
+ * divides, so the ring launches one kernel per computed block plus its
+ * staging copies.
  * With rope_theta > 0 every step's K block, the local one included, is
  * staged and rotated on the way (V is copied as is).
  * Blocks whose every pair is masked are still staged but not computed.
