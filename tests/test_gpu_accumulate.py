@@ -96,3 +96,29 @@ def test_invisible_block_leaves_the_state_unchanged():
     B.ra_block_attn_accumulate(q, kb[3], vb[3], 3, m=m, l=l, acc=a, **kw)  # future block
     torch.cuda.synchronize()
     assert torch.equal(m, m1) and torch.equal(l, l1) and torch.equal(a, a1)
+
+
+@pytest.mark.parametrize("layout,r", [("contiguous", 0), ("contiguous", 3), ("striped", 2)])
+def test_ring_final_divide_without_lse_and_against_finalize(layout, r):
+    """The ring's last computed launch divides in its epilogue: with lse not
+    requested the output is the same bits; and it equals the per-block
+    entry points followed by ra_finalize (the separate divide kernel), the
+    same arithmetic. Contiguous rank 0 computes only its own block, so there
+    the first launch is also the last."""
+    n, blen, hq, hkv, d = 4, 160, 8, 2, 64
+    say(f"final divide: {layout} r={r}")
+    qg, kg, vg = synth.random_global(43, 1, n * blen, hq, hkv, d, dtype="bf16", device=DEV)
+    q = qg[:, share_tokens(layout, n, r, blen).to(DEV)].contiguous()
+    kb, vb = blocks_from_global(kg, layout, n), blocks_from_global(vg, layout, n)
+    kw = dict(n_ring=n, rank=r, causal=True, layout=layout)
+    out, lse = B.ra_ring_fwd(q, kb, vb, **kw)
+    out2, lse2 = B.ra_ring_fwd(q, kb, vb, want_lse=False, **kw)
+    m, l, a = B.ra_block_attn_partial(q, kb[r], vb[r], r, **kw)
+    for s in range(1, n):
+        j = (r - s) % n
+        B.ra_block_attn_accumulate(q, kb[j], vb[j], j, m=m, l=l, acc=a, **kw)
+    o3, lse3 = B.ra_finalize(m, l, a)
+    torch.cuda.synchronize()
+    assert lse2 is None
+    assert torch.equal(out, out2)
+    assert torch.equal(out, o3) and torch.equal(lse, lse3)
