@@ -462,6 +462,62 @@ def backward_leg(dev, layouts, reps=1):
     return res
 
 
+def cu_scaling_leg(dev, n_wgs, kv=131072, d=128, seconds=4.0):
+    """Throughput per busy CU of the attention kernel against the number of
+    busy CUs: one non-causal 131072-key block of one KV head, 8-wave
+    workgroups of 256 query rows, q_len = 256 * n_wg rows, so a launch is
+    n_wg workgroups, one per CU (the LDS ring allows one per CU). Each count
+    runs back-to-back launches for `seconds` with the engine clock and
+    socket power sampled. Separates the kernel's efficiency per clock from
+    the clock the power limit leaves it."""
+    prev = os.environ.get("RA_WAVES")
+    os.environ["RA_WAVES"] = "8"   # the headline kernel's shape at every count
+    try:
+        g = torch.Generator(device=dev).manual_seed(3)
+        k = (0.5 * torch.randn(1, kv, 1, d, generator=g, device=dev)).to(torch.bfloat16)
+        v = torch.randn(1, kv, 1, d, generator=g, device=dev).to(torch.bfloat16)
+        res = []
+        for n_wg in n_wgs:
+            rows = 256 * n_wg
+            q = torch.randn(1, rows, 1, d, generator=g, device=dev).to(torch.bfloat16)
+            m = torch.empty(1, rows, 1, dtype=torch.float32, device=dev)
+            l = torch.empty_like(m)
+            acc = torch.empty(1, rows, 1, d, dtype=torch.float32, device=dev)
+
+            def f():
+                B.ra_block_attn_partial(q, k, v, 0, n_ring=1, rank=0, causal=False,
+                                        m=m, l=l, acc=acc)
+            f()
+            one = timed(f)
+            reps = max(3, int(seconds * 1e3 / one))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            sampler = ClockSampler()
+            with sampler:
+                e0.record()
+                for _ in range(reps):
+                    f()
+                e1.record()
+                e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            c = sampler.summary() or {}
+            tf = 4.0 * d * rows * kv / ms / 1e9
+            mhz = c.get("gfxclk_mhz_median")
+            per_cu_peak = PEAK_BF16_TFLOPS / 256 * ((mhz or ClockSampler.MAX_GFXCLK_MHZ) /
+                                                    ClockSampler.MAX_GFXCLK_MHZ)
+            res.append(dict(busy_cus=n_wg, ms=round(ms, 4), tflops=round(tf, 1),
+                            tflops_per_cu=round(tf / n_wg, 3), gfxclk_mhz=mhz,
+                            socket_power_w=c.get("socket_power_w_median"), reps=reps,
+                            frac_of_cu_peak_at_clock=round(tf / n_wg / per_cu_peak, 4)))
+            log(f"[bench] cu scaling {n_wg}: {res[-1]}")
+            del q, m, l, acc
+        return res
+    finally:
+        if prev is None:
+            os.environ.pop("RA_WAVES", None)
+        else:
+            os.environ["RA_WAVES"] = prev
+
+
 def load_counters(src_hash, kernel="attention"):
     """HBM traffic per launch of the attention kernel (or, kernel="merge", of
     the merge kernel) from committed rocprofv3 counter runs, only if they
@@ -500,6 +556,9 @@ def main():
     ap.add_argument("--overlap-only", action="store_true",
                     help="only the overlap leg of the workload's layouts (kernel-trace runs of "
                          "the staged ring against the no-copy sequence)")
+    ap.add_argument("--cu-scaling", default=None,
+                    help="comma list of busy-CU counts: only the attention kernel's throughput per "
+                         "busy CU against the number of busy CUs, with clock and power")
     ap.add_argument("--skip-aux", action="store_true",
                     help="no 8192-token overlap and no widened leg, so that every attention "
                          "launch has the headline workload's shape (kernel-trace runs)")
@@ -517,6 +576,10 @@ def main():
     torch.cuda.set_device(dev)
     if args.backward_only:
         print(json.dumps({"backward": backward_leg(dev, ["contiguous", "striped"])}), flush=True)
+        return
+    if args.cu_scaling:
+        counts = [int(x) for x in args.cu_scaling.split(",")]
+        print(json.dumps({"cu_scaling": cu_scaling_leg(dev, counts)}), flush=True)
         return
 
     c = synth.CONFIGS[args.workload]
