@@ -20,6 +20,10 @@ bandwidth of the standalone merge entry point, the backward ring, the other work
 921,600-token video share), and the fp64 CPU oracle timed on a bounded sample
 of the same workload (a reported baseline, not a target) together with the
 max-abs error of the GPU output on those sampled rows (`parity`).
+
+Separate runs: --backward-only (the backward leg), --overlap-only (the
+overlap leg, for kernel traces), --cu-scaling n1,n2,... (the attention
+kernel's throughput per busy CU against the number of busy CUs).
 """
 
 from __future__ import annotations
