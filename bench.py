@@ -15,8 +15,8 @@ Printed (one JSON line): TFLOP/s over causal-counted FLOPs (4*d per visible
 (its FLOPs per launch over its average launch time, measured with HIP events
 on its own stream), the cost of the staging copies (staged ring against the
 same kernels reading every block in place, interleaved pairs), the HBM
-bandwidth of the standalone merge entry point, the backward ring, the other workloads' ring TFLOP/s (the
-8192-token sequence, the 131072-token striped share at every rank, the
+bandwidth of the standalone merge entry point, the backward ring, the other
+workloads' ring TFLOP/s (the 8192-token sequence, the 131072-token striped share at every rank, the
 921,600-token video share), and the fp64 CPU oracle timed on a bounded sample
 of the same workload (a reported baseline, not a target) together with the
 max-abs error of the GPU output on those sampled rows (`parity`).
@@ -137,8 +137,10 @@ def ring_call(w, out, lse, ws, copy_stream="auto"):
 
 
 def kernel_leg(w):
-    """Attention kernel alone: one launch per computed block, HIP events on
-    the launch stream. Returns (total counted FLOPs, total ms, launches)."""
+    """Attention kernel alone, as the ring launches it: one launch per
+    computed block (the first writing the running state, the others merging
+    into it), HIP events on the launch stream. Returns (total counted FLOPs,
+    total ms, launches)."""
     c = w["cfg"]
     n, r, blen = c["n_ring"], w["rank"], c["block"]
     q = w["q"]
