@@ -101,7 +101,13 @@ class ClockSampler:
                 pass
             self._stop.wait(self.period_s)
 
+    # the firmware refreshes the metrics about once a second: a shorter
+    # region reads a stale value, so it reports none
+    MIN_SECONDS = 2.0
+
     def __enter__(self):
+        self._t0 = time.perf_counter()
+        self._t1 = None
         if self._smi is not None:
             import threading
             self._stop = threading.Event()
@@ -110,6 +116,7 @@ class ClockSampler:
         return self
 
     def __exit__(self, *exc):
+        self._t1 = time.perf_counter()
         if self._thread is not None:
             self._stop.set()
             self._thread.join()
@@ -117,6 +124,8 @@ class ClockSampler:
 
     def summary(self):
         if not self.samples:
+            return None
+        if self._t1 is not None and self._t1 - self._t0 < self.MIN_SECONDS:
             return None
         clks = sorted(c for c, _ in self.samples)
         pws = sorted(p for _, p in self.samples)
